@@ -1,0 +1,118 @@
+"""CPU oracle for packed variable-length attention forward (fp64).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the
+benchmark's CPU-baseline leg are the only callers. The HIP library never
+imports, links or calls anything here, and nothing here imports the HIP
+library or its binding.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, IEEE fp64, two-pass
+softmax); this module only compiles it with gcc and marshals numpy arrays.
+Parity pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle.py``
+(brute force on tiny inputs, a library special case, closed forms and
+invariants).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "attn_oracle.c"
+_LIB = _HERE / "liboracle.so"
+_lib = None
+
+
+def build(force: bool = True) -> Path:
+    """Compile the oracle with gcc into oracle/liboracle.so."""
+    if force or not _LIB.exists():
+        tmp = _LIB.with_suffix(".so.tmp")
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
+               "-o", str(tmp), str(_SRC), "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load_library(path) -> ctypes.CDLL:
+    """ctypes handle on a compiled oracle (the default build or a test variant)."""
+    lib = ctypes.CDLL(str(path))
+    f = lib.oracle_attn_varlen_fwd
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int32] * 3 + [ctypes.c_double,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int32]
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not _LIB.exists():
+            build(force=False)
+        _lib = load_library(_LIB)
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _bits(x) -> np.ndarray:
+    """bf16 input as a contiguous uint16 bit-pattern array (numpy or torch CPU)."""
+    if isinstance(x, np.ndarray):
+        if x.dtype != np.uint16:
+            raise TypeError("oracle expects bf16 bit patterns as uint16")
+        return np.ascontiguousarray(x)
+    import torch  # local: torch only used to accept CPU tensors
+
+    if x.dtype != torch.bfloat16 or x.device.type != "cpu":
+        raise TypeError("oracle expects a CPU bfloat16 tensor")
+    return np.ascontiguousarray(x.contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, rows=None,
+                    threads: int | None = None, library=None):
+    """fp64 attention for the given global query rows (all rows if None).
+
+    q: [Nq, H, D], k/v: [Nk, H, D] bf16 (uint16 bits or CPU bf16 tensors).
+    Returns (out [R, H, D] float64, lse [R, H] float64, natural log).
+    `library` selects another compiled oracle (tests use it for planted mistakes).
+    """
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    if qb.ndim != 3 or kb.shape != vb.shape or kb.ndim != 3:
+        raise ValueError("q must be [Nq,H,D] and k, v [Nk,H,D]")
+    _, H, D = qb.shape
+    if kb.shape[1:] != (H, D):
+        raise ValueError("head count / head dim mismatch")
+    cq = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int32))
+    ck = np.ascontiguousarray(np.asarray(cu_seqlens_k, dtype=np.int32))
+    B = len(cq) - 1
+    if len(ck) != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+    if B < 1 or cq[-1] > qb.shape[0] or ck[-1] > kb.shape[0]:
+        raise ValueError("cu_seqlens index past the q / k rows")
+    if rows is None:
+        r = None
+        nrows = int(cq[-1])
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = len(r)
+    out = np.zeros((nrows, H, D), dtype=np.float64)
+    lse = np.zeros((nrows, H), dtype=np.float64)
+    if nrows == 0:
+        return out, lse
+    lib = library if library is not None else _load()
+    rc = lib.oracle_attn_varlen_fwd(
+        qb.ctypes.data, kb.ctypes.data, vb.ctypes.data, cq.ctypes.data, ck.ctypes.data,
+        B, H, D, float(scale), None if r is None else r.ctypes.data, nrows,
+        out.ctypes.data, lse.ctypes.data, int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out, lse

@@ -1,0 +1,184 @@
+"""Seeded synthetic inputs for packed variable-length attention.
+
+This module draws random inputs and builds segment tables only; it holds none
+of the attention arithmetic. Both the HIP path (tests, benchmark) and the CPU
+oracle (tests) consume the bf16 tensors it returns, so how they are drawn never
+affects parity.
+
+Workloads (shapes taken from the pages; values are synthetic stand-ins because
+the pages' workloads are a private video model and a private training job):
+
+* ``dense_256``: one dense segment, S=256, H=2, D=64, N(0,1)*0.1.
+* ``varlen_cross``: the captured window call of the FA4 SM120 issue page
+  ("Bug 2 details"): 8 query segments summing to 35280 rows, H=56, D=128,
+  8 key/value segments of 17580 rows each, N(0,1)*0.1.
+* ``dense_77k``: S=77000, H=56, D=128, N(0,1): the length at which the NVFP4
+  path of the ffpa-attn PR #387 page aborts ("Minimal reproduction").
+* ``strided_9728``: N=410923 tokens in two segments [0,225304,410923], H=16,
+  D=96, N(0,1)*0.1, every tensor an [N,H,D] view of an [N,9728] buffer (the
+  cat([attn, mlp]) layout of the "_bwd_preprocess" overflow page).
+* ``dense_117k``: S=117000, H=56, D=128, N(0,1) (the ~117k-token generation
+  of the ffpa-attn page's "Verification").
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    num_heads: int
+    head_dim: int
+    cu_q: tuple
+    cu_k: tuple
+    std: float
+    self_attention: bool        # cu_q == cu_k, q/k/v drawn together
+    layout: str = "contiguous"  # or "stride9728"
+    outer_stride: int = 0       # elements per token row of the shared buffer
+    notes: str = field(default="", compare=False)
+
+    @property
+    def num_segments(self) -> int:
+        return len(self.cu_q) - 1
+
+    @property
+    def total_q(self) -> int:
+        return self.cu_q[-1]
+
+    @property
+    def total_k(self) -> int:
+        return self.cu_k[-1]
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return max((b - a for a, b in zip(self.cu_q[:-1], self.cu_q[1:])), default=0)
+
+    @property
+    def max_seqlen_k(self) -> int:
+        return max((b - a for a, b in zip(self.cu_k[:-1], self.cu_k[1:])), default=0)
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def flops(self) -> int:
+        """4 * Lq * Lk * D * H summed over segments (exact integer)."""
+        tot = 0
+        for b in range(self.num_segments):
+            lq = self.cu_q[b + 1] - self.cu_q[b]
+            lk = self.cu_k[b + 1] - self.cu_k[b]
+            tot += 4 * lq * lk * self.head_dim * self.num_heads
+        return tot
+
+    def algorithmic_bytes(self) -> int:
+        """Q, K, V and O in bf16 plus the fp32 LSE, each moved once."""
+        hd = self.num_heads * self.head_dim
+        return 2 * hd * (2 * self.total_q + 2 * self.total_k) + 4 * self.num_heads * self.total_q
+
+
+def _cu_uniform(n_seg: int, length: int) -> tuple:
+    return tuple(i * length for i in range(n_seg + 1))
+
+
+WORKLOADS = {
+    "dense_256": Workload("dense_256", 2, 64, (0, 256), (0, 256), 0.1, True),
+    "varlen_cross": Workload(
+        "varlen_cross", 56, 128,
+        (0, 4032, 9072, 14112, 19152, 24292, 29232, 34272, 35280),
+        _cu_uniform(8, 17580), 0.1, False),
+    "dense_77k": Workload("dense_77k", 56, 128, (0, 77000), (0, 77000), 1.0, True),
+    "strided_9728": Workload("strided_9728", 16, 96, (0, 225304, 410923), (0, 225304, 410923),
+                             0.1, True, layout="stride9728", outer_stride=9728),
+    "dense_117k": Workload("dense_117k", 56, 128, (0, 117000), (0, 117000), 1.0, True),
+}
+
+#: Canary written into the parts of an output buffer the kernel must not touch.
+CANARY = -1234.0  # exactly representable in bf16
+
+
+def custom(name: str, num_heads: int, head_dim: int, cu_q, cu_k=None, std: float = 0.1,
+           layout: str = "contiguous", outer_stride: int = 0) -> Workload:
+    cu_q = tuple(int(x) for x in cu_q)
+    self_attn = cu_k is None
+    cu_k = cu_q if cu_k is None else tuple(int(x) for x in cu_k)
+    return Workload(name, num_heads, head_dim, cu_q, cu_k, std, self_attn, layout, outer_stride)
+
+
+def _generator(device, seed: int) -> torch.Generator:
+    return torch.Generator(device=device).manual_seed(seed)
+
+
+def make_inputs(w: Workload, device="cuda", seed: int = 0, lse_head_pad: int = 0):
+    """Draw q, k, v for workload `w` and allocate out/lse.
+
+    Returns a dict with q, k, v, out (bf16 [tokens, H, D] views), lse (fp32
+    [H, total_q + lse_head_pad] with a canary tail), cu_q/cu_k (int32 tensors on
+    `device`) and `out_base` (the full buffer `out` lives in, canary-filled).
+    """
+    H, D = w.num_heads, w.head_dim
+    g = _generator(device, seed)
+    bf = torch.bfloat16
+    if w.layout == "stride9728":
+        if not w.self_attention:
+            raise ValueError("the strided layout is a self-attention layout")
+        S = w.outer_stride
+        if 3 * H * D > S:
+            raise ValueError("outer stride too small for q, k, v slices")
+        n = w.total_q
+        x = torch.empty((n, S), dtype=bf, device=device)
+        x.normal_(generator=g)
+        x.mul_(w.std)
+        hd = H * D
+        q = x[:, 0:hd].view(n, H, D)
+        k = x[:, hd:2 * hd].view(n, H, D)
+        v = x[:, 2 * hd:3 * hd].view(n, H, D)
+        y = torch.full((n, S), CANARY, dtype=bf, device=device)
+        out = y[:, 0:hd].view(n, H, D)
+        out_base = y
+    else:
+        if w.self_attention:
+            qkv = torch.randn((3, w.total_q, H, D), dtype=bf, device=device, generator=g)
+            if w.std != 1.0:
+                qkv.mul_(w.std)
+            q, k, v = qkv[0], qkv[1], qkv[2]
+        else:
+            q = torch.randn((w.total_q, H, D), dtype=bf, device=device, generator=g)
+            k = torch.randn((w.total_k, H, D), dtype=bf, device=device, generator=g)
+            v = torch.randn((w.total_k, H, D), dtype=bf, device=device, generator=g)
+            if w.std != 1.0:
+                q.mul_(w.std)
+                k.mul_(w.std)
+                v.mul_(w.std)
+        out_base = torch.full((w.total_q, H, D), CANARY, dtype=bf, device=device)
+        out = out_base
+    lse = torch.full((H, w.total_q + lse_head_pad), CANARY, dtype=torch.float32, device=device)
+    cu_q = torch.tensor(w.cu_q, dtype=torch.int32, device=device)
+    cu_k = torch.tensor(w.cu_k, dtype=torch.int32, device=device)
+    return {"q": q, "k": k, "v": v, "out": out, "out_base": out_base, "lse": lse,
+            "cu_q": cu_q, "cu_k": cu_k}
+
+
+def sample_rows(w: Workload, per_segment: int, seed: int = 0, edge: int = 64) -> list:
+    """Global query rows to compare: all rows of a segment when it has at most
+    `per_segment`; otherwise its first and last `edge` rows plus
+    `per_segment - 2*edge` distinct rows drawn from the rest (CPU generator,
+    one generator for all segments, segments in order)."""
+    g = torch.Generator().manual_seed(seed)
+    rows = []
+    for b in range(w.num_segments):
+        a, e = w.cu_q[b], w.cu_q[b + 1]
+        n = e - a
+        if n <= per_segment:
+            rows.extend(range(a, e))
+            continue
+        ed = min(edge, per_segment // 2)
+        mid = n - 2 * ed
+        pick = torch.randperm(mid, generator=g)[: per_segment - 2 * ed] + (a + ed)
+        rows.extend(range(a, a + ed))
+        rows.extend(sorted(int(x) for x in pick))
+        rows.extend(range(e - ed, e))
+    return rows
