@@ -1,0 +1,182 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed variable-length attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_77k]
+
+A step is one call of attn_varlen_fwd through the C ABI with cu_seqlens on the
+device: the cu read-back, the exact tile plan and the kernel launch. Inputs are
+resident in HBM before timing starts. Prints ONE JSON line on stdout:
+TFLOP/s with FLOPs = sum over segments of 4*Lq*Lk*D*H, the kernel's roofline
+figures (its own average duration from HIP events on the launch stream), and
+the CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+KERNEL_SOURCES = ["varlen_flashattention_forward_amd/csrc/avf_kernel.hip",
+                  "varlen_flashattention_forward_amd/csrc/avf_plan.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update((ROOT / p).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    f = ROOT / "profiles" / f"traffic_avf_fwd_{workload}.json"
+    if not f.exists():
+        return None
+    d = json.loads(f.read_text())
+    if d.get("kernel_hash") != kernel_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, t, rows_per_segment: int):
+    import numpy as np
+
+    import oracle
+    from varlen_flashattention_forward_amd.workloads import sample_rows
+
+    rows = sample_rows(w, rows_per_segment, edge=min(8, rows_per_segment // 2))
+    q, k, v = (t[n].contiguous().cpu() for n in ("q", "k", "v"))
+    threads = oracle.default_threads()
+    flops = 0
+    import bisect
+    for r in rows:
+        b = bisect.bisect_right(w.cu_q, r) - 1
+        flops += 4 * (w.cu_k[b + 1] - w.cu_k[b]) * w.head_dim * w.num_heads
+    t0 = time.perf_counter()
+    oracle.attn_varlen_fwd(q, k, v, w.cu_q, w.cu_k, float(np.float32(w.softmax_scale)), rows=rows,
+                           threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} query rows x {w.num_heads} heads of {w.name} against their full key "
+                      f"segments (C fp64 oracle, {dt:.1f} s, {flops / 1e9:.1f} GFLOP)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense_77k")
+    ap.add_argument("--cpu-rows", type=int, default=8, help="query rows per segment for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the library runs on a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import varlen_flashattention_forward_amd as avf
+    from varlen_flashattention_forward_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    avf.lib()
+    log(f"[bench] workload {w.name}: H={w.num_heads} D={w.head_dim} segments={w.num_segments} "
+        f"total_q={w.total_q} total_k={w.total_k}")
+    t = make_inputs(w, dev, seed=0)
+    torch.cuda.synchronize()
+    flops = w.flops()
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        avf.attn_varlen_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                            softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / args.steps * 1e3
+    value = flops / (ms / 1e3) / 1e12
+    log(f"[bench] {args.steps} steps: {ms:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    # kernel-only duration: HIP events on the launch stream around the launch
+    # (host cu_seqlens entry: no read-back inside the bracket)
+    cu_q, cu_k = list(w.cu_q), list(w.cu_k)
+    durs = []
+    for _ in range(args.steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        avf.attn_varlen_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                            softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"],
+                            cu_seqlens_q_host=cu_q, cu_seqlens_k_host=cu_k, stream=stream.cuda_stream)
+        e1.record(stream)
+        durs.append((e0, e1))
+    torch.cuda.synchronize()
+    kms = sum(a.elapsed_time(b) for a, b in durs) / len(durs)
+    launches, wgs = avf.grid_plan(w.cu_q, w.num_heads, w.head_dim)
+    achieved = flops / launches / (kms / launches / 1e3) / 1e12
+    log(f"[bench] kernel: {kms:.3f} ms/call over {launches} launch(es), {wgs} workgroups, {achieved:.1f} TFLOP/s")
+    traffic = traffic_for(w.name)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel_ms": round(kms / launches, 4), "algorithmic_flops_per_launch": flops // launches,
+                "algorithmic_bytes_per_launch": w.algorithmic_bytes() // launches}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline ...")
+        cpu = cpu_baseline(w, t, args.cpu_rows)
+        log(f"[bench] cpu baseline {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+
+    rec = {
+        "metric": "attention fwd TFLOP/s (4*Sq*Sk*D*H) and % of MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": w.name, "num_heads": w.num_heads, "head_dim": w.head_dim,
+                   "segments": w.num_segments, "total_q": w.total_q, "total_k": w.total_k,
+                   "max_seqlen_q": w.max_seqlen_q, "max_seqlen_k": w.max_seqlen_k,
+                   "layout": w.layout, "causal": False, "flops_per_step": flops,
+                   "workgroups": wgs, "block_m": avf.block_m(w.head_dim)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,177 @@
+/*
+ * attn_varlen.h: C ABI of the MI355X (gfx950) packed variable-length
+ * attention forward library (libattn_varlen.so).
+ *
+ * Operation. For every segment b, with query rows [cu_q[b], cu_q[b+1]) and
+ * key/value rows [cu_k[b], cu_k[b+1]), every head h and every query row i of
+ * the segment:
+ *     O[i,h,:] = softmax_j(scale * Q[i,h,:] . K[j,h,:]) V[j,h,:]   (j in segment b)
+ *     LSE[h,i] = ln sum_j exp(scale * Q[i,h,:] . K[j,h,:])
+ * This is the varlen flash-attention forward with its (out, lse) return as
+ * used on the "[FA4] cute varlen backward: int32 overflow in _bwd_preprocess
+ * ..." page ("Real-world trigger", repro script forward call) and the
+ * "[FA4][SM120] flash_attn_varlen_func ... illegal memory access at >=4 varlen
+ * segments" page ("Bug 2 details": packed q [35280,56,128], cu_seqlens_q,
+ * max_seqlen_q/k). Non-causal; equal head counts for Q and K/V.
+ *
+ * Layout. q, out: [total_q, H, D]; k, v: [total_k, H, D]; bf16; the D
+ * dimension is contiguous (stride 1); the token-row and head strides are free
+ * (in ELEMENTS, int64), e.g. the [N,H,D] views with row stride 9728 of the
+ * _bwd_preprocess page. lse: fp32, element (h, i) at lse[h*lse_head + i].
+ * Every offset is formed in 64-bit arithmetic, so element offsets past 2^31
+ * and byte offsets past 2^32 are fine (that page's "Verified sample":
+ * 225304 * 9728 = 2,191,757,312 must not wrap).
+ *
+ * Ownership. The caller owns every buffer and the stream. The library keeps
+ * no pointer after a call returns, allocates no device memory and launches
+ * work only on the given stream (asynchronously). out/lse must not overlap
+ * q/k/v element-wise.
+ *
+ * Errors. Every entry point returns 0 on success or a negative
+ * ATTN_VARLEN_E* code; nothing asserts or aborts. Invalid arguments are
+ * rejected on the host before any HIP call, so an error never leaves work
+ * queued. attn_varlen_last_error() gives a message for the calling thread.
+ */
+#ifndef ATTN_VARLEN_H
+#define ATTN_VARLEN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_VARLEN_OK 0
+#define ATTN_VARLEN_ENULL (-1)        /* a required pointer is NULL */
+#define ATTN_VARLEN_EINVAL (-2)       /* bad count, stride, scale or overlapping output */
+#define ATTN_VARLEN_EUNSUPPORTED (-3) /* head_dim not in {64, 96, 128}, stride over limit */
+#define ATTN_VARLEN_EALIGN (-4)       /* pointer not 16-byte aligned / stride not a multiple of 8 */
+#define ATTN_VARLEN_ECU (-5)          /* cu_seqlens: cu[0] != 0, decreasing, or past the token extents */
+#define ATTN_VARLEN_EMAXSEQ (-6)      /* a segment is longer than max_seqlen_q / max_seqlen_k */
+#define ATTN_VARLEN_EHIP (-7)         /* HIP runtime or launch failure */
+
+/* Largest token-row stride accepted, in elements (8 MiB rows). */
+#define ATTN_VARLEN_MAX_ROW_STRIDE (1LL << 22)
+
+/*
+ * Tensor layout. Strides are in ELEMENTS; the innermost (D) stride is always
+ * 1. The token extents let the library refuse cu_seqlens that would index
+ * past the caller's buffers.
+ */
+typedef struct attn_varlen_layout {
+    int64_t q_row, q_head;
+    int64_t k_row, k_head;
+    int64_t v_row, v_head;
+    int64_t o_row, o_head;
+    int64_t lse_head; /* lse[h*lse_head + i]; 0 selects q_tokens */
+    int64_t q_tokens; /* token rows addressable in q and out; cu_q[B] <= q_tokens */
+    int64_t k_tokens; /* token rows addressable in k and v; cu_k[B] <= k_tokens */
+} attn_varlen_layout;
+
+/*
+ * Varlen attention forward with cu_seqlens in DEVICE memory (int32, B+1
+ * entries each), the calling form of flash_attn_varlen_func on both FA4
+ * pages. The library copies the 2*(B+1) integers to the host on `stream` and
+ * waits for them (the one synchronisation of the call), checks them, plans an
+ * exact grid (one workgroup per (segment, query block, head) tile; no spare
+ * blocks, cf. the over-provisioned SingleTileVarlenScheduler grid of the SM120
+ * page's "Interpretation") and launches.
+ *
+ *   q, k, v        bf16 device pointers, 16-byte aligned (q/out may be NULL
+ *                  when q_tokens == 0, k/v when k_tokens == 0).
+ *   cu_seqlens_q/k int32 device arrays of num_segments+1 cumulative offsets.
+ *   num_segments   B >= 0 (B == 0 is a no-op).
+ *   num_heads      H >= 1; head_dim D in {64, 96, 128}.
+ *   max_seqlen_q/k upper bounds on segment lengths (checked, never trusted).
+ *   layout         element strides and token extents (attn_varlen_layout);
+ *                  head strides >= 0, row strides in [1,
+ *                  ATTN_VARLEN_MAX_ROW_STRIDE], all multiples of 8; out must
+ *                  not overlap itself; lse_head >= cu_q[B] when H > 1.
+ *   softmax_scale  finite and > 0 (1/sqrt(D) in the pages' configurations).
+ *   out            bf16 device pointer, [total_q, H, D] under o_row/o_head.
+ *   lse            fp32 device pointer or NULL (no LSE written).
+ *   stream         hipStream_t, or NULL for the null stream.
+ * Query rows of a segment with no keys get O = 0 and LSE = -inf.
+ */
+int32_t attn_varlen_fwd(const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int32_t num_segments, int32_t num_heads, int32_t head_dim,
+                        int32_t max_seqlen_q, int32_t max_seqlen_k,
+                        const attn_varlen_layout* layout, float softmax_scale,
+                        void* out, float* lse, void* stream);
+
+/*
+ * Same operation with cu_seqlens in HOST memory: no device-to-host copy and
+ * no synchronisation, so the call only enqueues work on `stream`. The host
+ * arrays are read during the call and not kept.
+ */
+int32_t attn_varlen_fwd_hostcu(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_q_host,
+                               const int32_t* cu_seqlens_k_host, int32_t num_segments,
+                               int32_t num_heads, int32_t head_dim, int32_t max_seqlen_q,
+                               int32_t max_seqlen_k, const attn_varlen_layout* layout,
+                               float softmax_scale, void* out, float* lse, void* stream);
+
+/*
+ * Argument check of attn_varlen_fwd_hostcu without any HIP call: returns the
+ * code that call would return before launching. Pointers are only checked
+ * for NULL and alignment, never dereferenced (cu arrays are host arrays).
+ */
+int32_t attn_varlen_validate(const void* q, const void* k, const void* v,
+                             const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_k_host,
+                             int32_t num_segments, int32_t num_heads, int32_t head_dim,
+                             int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             const attn_varlen_layout* layout, float softmax_scale,
+                             const void* out, const float* lse);
+
+/*
+ * Query rows per tile (BM) the library uses for head_dim, or
+ * ATTN_VARLEN_EUNSUPPORTED.
+ */
+int32_t attn_varlen_block_m(int32_t head_dim);
+
+/*
+ * Exact tile count H * sum_b ceil(Lq_b / block_m) for host cu_seqlens_q
+ * (the per-segment-ceil accounting of the SM120 page's "Interpretation").
+ * Returns a negative code on bad arguments (block_m <= 0, H <= 0, bad cu).
+ */
+int64_t attn_varlen_count_tiles(const int32_t* cu_seqlens_q_host, int32_t num_segments,
+                                int32_t num_heads, int32_t block_m);
+
+/*
+ * Number of kernel launches and workgroups attn_varlen_fwd would use for
+ * these host cu_seqlens (segments are split into launches of at most
+ * attn_varlen_segments_per_launch() segments; each launch's grid is exactly
+ * its tile count). Writes the totals to *launches and *workgroups.
+ */
+int32_t attn_varlen_grid_plan(const int32_t* cu_seqlens_q_host, int32_t num_segments,
+                              int32_t num_heads, int32_t head_dim, int64_t* launches,
+                              int64_t* workgroups);
+int32_t attn_varlen_segments_per_launch(void);
+
+/*
+ * Tile decode used by the kernel, exposed for host-side tests: for a launch
+ * covering segments with host cu_seqlens_q (B+1 entries, B <= segments per
+ * launch), maps workgroup index `wg` to (segment, query block, head).
+ * Returns 0, or a negative code when wg is outside the exact grid.
+ */
+int32_t attn_varlen_decode_tile(const int32_t* cu_seqlens_q_host, int32_t num_segments,
+                                int32_t num_heads, int32_t block_m, int64_t wg,
+                                int32_t* segment, int32_t* q_block, int32_t* head);
+
+/*
+ * Element offset row*row_stride + head*head_stride as the kernel forms it
+ * (int64 throughout), exposed so tests can pin it against the wrap values of
+ * the _bwd_preprocess page's "Verified sample".
+ */
+int64_t attn_varlen_element_offset(int64_t row, int64_t row_stride, int64_t head,
+                                   int64_t head_stride);
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+const char* attn_varlen_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_VARLEN_H */

@@ -1,0 +1,222 @@
+"""Host-side tests of libattn_varlen.so: exported symbols, argument checks,
+64-bit offset arithmetic and the exact tile plan. No GPU needed: nothing here
+launches a kernel or touches device memory.
+"""
+import ctypes
+import json
+import math
+import random
+import re
+from pathlib import Path
+
+import pytest
+
+import varlen_flashattention_forward_amd as avf
+from varlen_flashattention_forward_amd import _binding
+from varlen_flashattention_forward_amd.workloads import WORKLOADS
+
+ROOT = Path(__file__).resolve().parents[1]
+GOLDEN = json.loads((ROOT / "tests" / "golden" / "pages_integers.json").read_text())
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not _binding.LIB_PATH.exists():
+        from varlen_flashattention_forward_amd import build
+        build.build()
+    avf.lib()
+
+
+def header_functions():
+    text = (ROOT / "include" / "attn_varlen.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_varlen_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(str(_binding.LIB_PATH))
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/attn_varlen.h but not exported"
+    assert sorted(_binding.EXPORTED_SYMBOLS) == names
+
+
+# ------------------------------------------------------------ 64-bit offsets (pages' numbers)
+
+def test_offset_matches_pages_verified_sample():
+    g = GOLDEN["offset_wrap"]
+    off = avf.element_offset(g["coord"], g["row_stride"], 0, 0)
+    assert off == g["true_offset"] == 2_191_757_312
+    # what an int32 accumulator would have produced, per the page, is not what we form
+    wrapped = (off + 2**31) % 2**32 - 2**31
+    assert wrapped == g["offset_as_signed_i32"]
+    assert wrapped % 2**64 == g["offset_sign_extended_u64"]
+    assert off != wrapped
+    parts = g["row_stride_parts"]
+    assert parts["heads"] * parts["head_dim"] + parts["mlp_dim"] == g["row_stride"]
+
+
+def test_offset_threshold_and_largest_strided_offset():
+    g = GOLDEN["offset_wrap"]
+    t = g["wrap_threshold_approx"]
+    assert avf.element_offset(t, g["row_stride"], 0, 0) >= 2**31
+    assert avf.element_offset(t - 1, g["row_stride"], 0, 0) < 2**31
+    # last element of the strided layout: row N-1, head 15, plus the 3rd slice (v) offset
+    n = g["total_tokens"]
+    last = avf.element_offset(n - 1, 9728, 15, 96) + 2 * 1536 + 95
+    assert last == (n - 1) * 9728 + 15 * 96 + 3072 + 95
+    assert last * 2 > 2**32          # byte offsets past 2^32 as well
+    # head offsets combine in 64 bits too
+    assert avf.element_offset(3, 1 << 22, (1 << 31) - 1, 1 << 22) == 3 * (1 << 22) + ((1 << 31) - 1) * (1 << 22)
+
+
+# ------------------------------------------------------------ exact tile accounting
+
+def test_tile_count_matches_pages_valid_tiles():
+    g = GOLDEN["varlen_grid"]
+    assert avf.count_tiles(g["cu_seqlens_q"], g["num_heads"], g["tile_m"]) == g["valid_tiles"]
+    # the variant with every middle window 5040 rows has the same count
+    cu2 = list(g["cu_seqlens_q"])
+    cu2[5] = 24192
+    assert avf.count_tiles(cu2, g["num_heads"], g["tile_m"]) == g["valid_tiles"]
+
+
+def test_our_grid_is_exact_for_every_workload():
+    for w in WORKLOADS.values():
+        bm = avf.block_m(w.head_dim)
+        exact = w.num_heads * sum(math.ceil((b - a) / bm) for a, b in zip(w.cu_q[:-1], w.cu_q[1:]))
+        launches, wgs = avf.grid_plan(w.cu_q, w.num_heads, w.head_dim)
+        assert wgs == exact == avf.count_tiles(w.cu_q, w.num_heads, bm)
+        assert launches == 1
+
+
+def test_grid_plan_splits_long_segment_lists():
+    spl = avf.segments_per_launch()
+    rng = random.Random(0)
+    lens = [rng.choice([0, 1, 7, 64, 255, 256, 257, 1000]) for _ in range(3 * spl + 5)]
+    cu = [0]
+    for x in lens:
+        cu.append(cu[-1] + x)
+    launches, wgs = avf.grid_plan(cu, 3, 128)
+    bm = avf.block_m(128)
+    assert wgs == 3 * sum(math.ceil(x / bm) for x in lens)
+    assert launches == math.ceil(len(lens) / spl)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_is_a_bijection_onto_valid_tiles(seed):
+    rng = random.Random(seed)
+    B = rng.randint(1, avf.segments_per_launch())
+    H = rng.choice([1, 2, 3, 8, 56])
+    bm = rng.choice([64, 128, 256])
+    cu = [0]
+    for _ in range(B):
+        cu.append(cu[-1] + rng.choice([0, 0, 1, bm - 1, bm, bm + 1, rng.randint(1, 5 * bm)]))
+    T = avf.count_tiles(cu, H, bm)
+    seen = set()
+    for wg in range(T):
+        s, m, h = avf.decode_tile(cu, H, bm, wg)
+        lq = cu[s + 1] - cu[s]
+        assert lq > 0 and 0 <= m < math.ceil(lq / bm) and 0 <= h < H
+        seen.add((s, m, h))
+    assert len(seen) == T
+    if T:
+        with pytest.raises(avf.AttnVarlenError):
+            avf.decode_tile(cu, H, bm, T)   # no workgroup beyond the exact grid
+
+
+def test_first_block_past_the_pages_grid_is_outside_ours():
+    g = GOLDEN["varlen_grid"]
+    with pytest.raises(avf.AttnVarlenError):
+        avf.decode_tile(g["cu_seqlens_q"], g["num_heads"], g["tile_m"], g["first_faulting_block"])
+    avf.decode_tile(g["cu_seqlens_q"], g["num_heads"], g["tile_m"], g["first_faulting_block"] - 1)
+
+
+# ------------------------------------------------------------ argument checks (no HIP calls)
+
+P = 1 << 20  # a 16-byte-aligned fake address; validate never dereferences it
+
+
+def layout(H=2, D=64, nq=10, nk=12, **kw):
+    base = dict(q_row=H * D, q_head=D, k_row=H * D, k_head=D, v_row=H * D, v_head=D,
+                o_row=H * D, o_head=D, lse_head=0, q_tokens=nq, k_tokens=nk)
+    base.update(kw)
+    return _binding.Layout(**base)
+
+
+def v(cu_q=(0, 4, 10), cu_k=(0, 5, 12), H=2, D=64, max_q=6, max_k=7, lay=None, scale=0.125,
+      q=P, k=P, vv=P, out=P, lse=P):
+    lay = lay or layout(H, D)
+    return avf.validate(q, k, vv, list(cu_q), list(cu_k), H, D, max_q, max_k, lay, scale, out, lse)
+
+
+def test_validate_accepts_good_arguments():
+    assert v() == 0
+    assert v(lse=None) == 0
+    assert v(D=96, lay=layout(D=96)) == 0 and v(D=128, lay=layout(D=128)) == 0
+    # strided view of a wider buffer (row stride 9728, head stride 96)
+    lay = layout(H=16, D=96, q_row=9728, q_head=96, k_row=9728, k_head=96, v_row=9728, v_head=96,
+                 o_row=9728, o_head=96)
+    assert v(H=16, D=96, lay=lay) == 0
+    # [H, S, D] layout: head stride larger than row stride
+    lay = layout(q_row=64, q_head=640, k_row=64, k_head=768, v_row=64, v_head=768, o_row=64, o_head=640)
+    assert v(lay=lay) == 0
+    # empty segments are fine, B = 0 is a no-op
+    assert v(cu_q=(0, 0, 10), cu_k=(0, 5, 5), max_q=10) == 0
+    assert avf.validate(None, None, None, [0], [0], 2, 64, 0, 0, layout(), 0.125, None, None) == 0
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), _binding.ENULL),
+    (dict(out=None), _binding.ENULL),
+    (dict(H=0), _binding.EINVAL),
+    (dict(D=80, lay=layout(D=80)), _binding.EUNSUPPORTED),
+    (dict(D=256, lay=layout(D=256)), _binding.EUNSUPPORTED),
+    (dict(scale=0.0), _binding.EINVAL),
+    (dict(scale=-1.0), _binding.EINVAL),
+    (dict(scale=float("nan")), _binding.EINVAL),
+    (dict(scale=float("inf")), _binding.EINVAL),
+    (dict(q=P + 8), _binding.EALIGN),
+    (dict(out=P + 2), _binding.EALIGN),
+    (dict(lse=P + 2), _binding.EALIGN),
+    (dict(lay=layout(k_row=132)), _binding.EALIGN),
+    (dict(lay=layout(v_head=60)), _binding.EALIGN),
+    (dict(lay=layout(q_row=0)), _binding.EINVAL),
+    (dict(lay=layout(o_head=-64)), _binding.EINVAL),
+    (dict(lay=layout(k_row=(1 << 22) + 8)), _binding.EUNSUPPORTED),
+    (dict(cu_q=(1, 4, 10)), _binding.ECU),
+    (dict(cu_k=(0, 6, 5)), _binding.ECU),
+    (dict(cu_q=(0, 4, 11), max_q=7), _binding.ECU),   # past q_tokens = 10
+    (dict(cu_k=(0, 5, 13), max_k=8), _binding.ECU),   # past k_tokens = 12
+    (dict(max_q=5), _binding.EMAXSEQ),
+    (dict(max_k=6), _binding.EMAXSEQ),
+    (dict(max_q=-1), _binding.EINVAL),
+    (dict(lay=layout(o_row=64, o_head=64)), _binding.EINVAL),      # out rows and heads alias
+    (dict(lay=layout(o_row=120, o_head=64)), _binding.EINVAL),     # rows overlap within a head
+    (dict(lay=layout(lse_head=8)), _binding.EINVAL),               # lse heads overlap
+])
+def test_validate_rejects(kwargs, code):
+    rc = v(**kwargs)
+    assert rc == code, (rc, avf.last_error())
+    assert avf.last_error()
+
+
+def test_validate_never_needs_lse_head_with_one_head():
+    assert v(H=1, lay=layout(H=1, lse_head=1)) == 0
+
+
+def test_block_m_and_unsupported_dims():
+    for d in (64, 96, 128):
+        bm = avf.block_m(d)
+        assert bm > 0 and bm % 32 == 0
+    with pytest.raises(avf.AttnVarlenError):
+        avf.block_m(100)
+
+
+def test_forward_rejects_cpu_tensors_before_any_hip_call():
+    import torch
+    q = torch.zeros((4, 2, 64), dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        avf.attn_varlen_fwd(q, q, q, cu, cu, 4, 4)

@@ -17,6 +17,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import blas_oracle
 
 ROOT = Path(__file__).resolve().parents[1]
 
@@ -84,19 +85,40 @@ def sdpa_reference(q, k, v, cu_q, cu_k, scale):
     return out.numpy(), lse.numpy()
 
 
-def run(q, k, v, cu_q, cu_k, scale, rows=None, library=None, threads=4):
-    return oracle.attn_varlen_fwd(q, k, v, cu_q, cu_k, scale, rows=rows, threads=threads, library=library)
+def c_oracle(library=None):
+    """The C oracle (default build, or a planted-mistake build) as a callable."""
+    def F(q, k, v, cu_q, cu_k, scale, rows=None, threads=4):
+        return oracle.attn_varlen_fwd(q, k, v, cu_q, cu_k, scale, rows=rows, threads=threads,
+                                      library=library)
+    F.bitwise = True   # row results do not depend on which other rows are evaluated
+    return F
 
 
-# ---------------------------------------------------------------- pins (each takes a library)
+def blas_oracle_fn(q, k, v, cu_q, cu_k, scale, rows=None, threads=None):
+    return blas_oracle.attn_varlen_fwd(q, k, v, cu_q, cu_k, scale, rows=rows, row_chunk=3)
 
-def pin_brute_force(library):
+
+# a BLAS product's rounding may depend on the operand shapes, so row results
+# can differ in the last bits with the set of rows evaluated together
+blas_oracle_fn.bitwise = False
+
+
+def same(F, a, b):
+    if F.bitwise:
+        return np.array_equal(a, b)
+    fa, fb = np.isfinite(a), np.isfinite(b)
+    return np.array_equal(fa, fb) and np.array_equal(a[~fa], b[~fb]) and np.allclose(a[fa], b[fb], rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- pins (each takes an oracle callable)
+
+def pin_brute_force(F):
     rng = np.random.default_rng(1)
     for cu_q, cu_k, H, D in [([0, 3, 3, 9], [0, 5, 6, 6], 2, 8), ([0, 7], [0, 4], 1, 4),
                              ([0, 1, 4], [0, 9, 11], 2, 6)]:
         q, k, v = rand_case(rng, cu_q, cu_k, H, D)
         scale = 1.0 / math.sqrt(D)
-        o, l = run(q, k, v, cu_q, cu_k, scale, library=library)
+        o, l = F(q, k, v, cu_q, cu_k, scale)
         bo, bl = brute_force(q, k, v, cu_q, cu_k, scale)
         np.testing.assert_allclose(o, bo, rtol=1e-12, atol=1e-13)
         fin = np.isfinite(bl)
@@ -105,14 +127,14 @@ def pin_brute_force(library):
         assert np.all(l[~fin] == -np.inf)
 
 
-def pin_small_integers(library):
+def pin_small_integers(F):
     """Small-integer inputs: scores are exact, so O and LSE follow from a few
     exponentials; compare with Python's own math on exact rationals."""
     from fractions import Fraction
     q = to_bf16_bits([[[1, 0]], [[0, 2]]])          # 2 rows, H=1, D=2
     k = to_bf16_bits([[[1, 1]], [[2, -1]], [[0, 1]]])
     v = to_bf16_bits([[[3, 0]], [[0, 5]], [[1, 1]]])
-    o, l = run(q, k, v, [0, 2], [0, 3], 1.0, library=library)
+    o, l = F(q, k, v, [0, 2], [0, 3], 1.0)
     for i, qi in enumerate(([1, 0], [0, 2])):
         s = [qi[0] * kk[0] + qi[1] * kk[1] for kk in ([1, 1], [2, -1], [0, 1])]
         w = [math.exp(x) for x in s]
@@ -123,23 +145,23 @@ def pin_small_integers(library):
     assert Fraction(1)  # (exact scores: integers)
 
 
-def pin_sdpa(library):
+def pin_sdpa(F):
     rng = np.random.default_rng(2)
     cu_q, cu_k, H, D = [0, 300, 700, 1000], [0, 500, 510, 1300], 2, 64
     q, k, v = rand_case(rng, cu_q, cu_k, H, D, std=1.0)
     scale = 1.0 / math.sqrt(D)
-    o, l = run(q, k, v, cu_q, cu_k, scale, library=library)
+    o, l = F(q, k, v, cu_q, cu_k, scale)
     so, sl = sdpa_reference(q, k, v, cu_q, cu_k, scale)
     np.testing.assert_allclose(o, so, rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(l, sl, rtol=1e-12, atol=1e-12)
 
 
-def pin_closed_forms(library):
+def pin_closed_forms(F):
     rng = np.random.default_rng(3)
     H, D = 2, 8
     # one key: O = v0, LSE = s0
     q, k, v = rand_case(rng, [0, 4], [0, 1], H, D)
-    o, l = run(q, k, v, [0, 4], [0, 1], 0.5, library=library)
+    o, l = F(q, k, v, [0, 4], [0, 1], 0.5)
     vf, qf, kf = bits_to_f64(v), bits_to_f64(q), bits_to_f64(k)
     for i in range(4):
         for h in range(H):
@@ -149,18 +171,18 @@ def pin_closed_forms(library):
     # Q = 0: O = mean(V), LSE = ln(Lk)
     q0 = to_bf16_bits(np.zeros((3, H, D)))
     _, k, v = rand_case(rng, [0, 3], [0, 7], H, D)
-    o, l = run(q0, k, v, [0, 3], [0, 7], 0.3, library=library)
+    o, l = F(q0, k, v, [0, 3], [0, 7], 0.3)
     np.testing.assert_allclose(o, np.broadcast_to(bits_to_f64(v).mean(axis=0), o.shape), rtol=1e-14, atol=1e-15)
     np.testing.assert_allclose(l, math.log(7), rtol=1e-15)
     # V constant per head: O = that constant
     q, k, _ = rand_case(rng, [0, 5], [0, 6], H, D)
     vc = to_bf16_bits(np.broadcast_to(np.array([0.75, -2.5])[None, :, None], (6, H, D)))
-    o, _ = run(q, k, vc, [0, 5], [0, 6], 0.25, library=library)
+    o, _ = F(q, k, vc, [0, 5], [0, 6], 0.25)
     np.testing.assert_allclose(o[:, 0], 0.75, rtol=1e-14)
     np.testing.assert_allclose(o[:, 1], -2.5, rtol=1e-14)
     # two keys: O = sigmoid(s0 - s1) v0 + sigmoid(s1 - s0) v1
     q, k, v = rand_case(rng, [0, 4], [0, 2], H, D)
-    o, l = run(q, k, v, [0, 4], [0, 2], 0.7, library=library)
+    o, l = F(q, k, v, [0, 4], [0, 2], 0.7)
     qf, kf, vf = bits_to_f64(q), bits_to_f64(k), bits_to_f64(v)
     for i in range(4):
         for h in range(H):
@@ -172,12 +194,12 @@ def pin_closed_forms(library):
             assert abs(l[i, h] - exp_l) <= 1e-12 * max(1.0, abs(exp_l))
     # empty key segment: O = 0, LSE = -inf; other segment unaffected
     q, k, v = rand_case(rng, [0, 2, 5], [0, 0, 4], H, D)
-    o, l = run(q, k, v, [0, 2, 5], [0, 0, 4], 0.4, library=library)
+    o, l = F(q, k, v, [0, 2, 5], [0, 0, 4], 0.4)
     assert np.all(o[:2] == 0) and np.all(l[:2] == -np.inf)
     assert np.all(np.isfinite(l[2:]))
 
 
-def pin_needle(library):
+def pin_needle(F):
     """q = alpha * k_t with a large alpha: softmax is one-hot at t, O = v_t.
     Also large logits (|s| ~ 1e3) must not overflow."""
     rng = np.random.default_rng(4)
@@ -186,50 +208,50 @@ def pin_needle(library):
     v = to_bf16_bits(rng.standard_normal((nk, H, D)))
     for t in (0, 5, nk - 1):
         q = to_bf16_bits(64.0 * bits_to_f64(k)[t:t + 1])
-        o, l = run(q, k, v, [0, 1], [0, nk], 1.0, library=library)
+        o, l = F(q, k, v, [0, 1], [0, nk], 1.0)
         np.testing.assert_allclose(o[0, 0], bits_to_f64(v)[t, 0], rtol=0, atol=1e-6)
         assert abs(l[0, 0] - 64.0 * D) < 1e-6
         assert np.all(np.isfinite(o))
 
 
-def pin_invariants(library):
+def pin_invariants(F):
     rng = np.random.default_rng(5)
     cu_q, cu_k, H, D = [0, 6, 13, 20], [0, 9, 10, 25], 2, 16
     q, k, v = rand_case(rng, cu_q, cu_k, H, D)
     scale = 0.25
-    o, l = run(q, k, v, cu_q, cu_k, scale, library=library)
+    o, l = F(q, k, v, cu_q, cu_k, scale)
     # key permutation within a segment (k and v rows together)
     perm = np.concatenate([rng.permutation(np.arange(a, b)) for a, b in zip(cu_k[:-1], cu_k[1:])])
-    op, lp = run(q, k[perm], v[perm], cu_q, cu_k, scale, library=library)
+    op, lp = F(q, k[perm], v[perm], cu_q, cu_k, scale)
     np.testing.assert_allclose(op, o, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(lp, l, rtol=1e-12, atol=1e-14)
     # segment independence: other segments' data changed, segment 1 bitwise equal
     q2, k2, v2 = rand_case(rng, cu_q, cu_k, H, D)
     q2[6:13], k2[9:10], v2[9:10] = q[6:13], k[9:10], v[9:10]
-    o2, l2 = run(q2, k2, v2, cu_q, cu_k, scale, library=library)
-    assert np.array_equal(o2[6:13], o[6:13]) and np.array_equal(l2[6:13], l[6:13])
+    o2, l2 = F(q2, k2, v2, cu_q, cu_k, scale)
+    assert same(F, o2[6:13], o[6:13]) and same(F, l2[6:13], l[6:13])
     # packed == per-segment runs
     for b in range(3):
-        ob, lb = run(q[cu_q[b]:cu_q[b + 1]], k[cu_k[b]:cu_k[b + 1]], v[cu_k[b]:cu_k[b + 1]],
-                     [0, cu_q[b + 1] - cu_q[b]], [0, cu_k[b + 1] - cu_k[b]], scale, library=library)
-        assert np.array_equal(ob, o[cu_q[b]:cu_q[b + 1]]) and np.array_equal(lb, l[cu_q[b]:cu_q[b + 1]])
+        ob, lb = F(q[cu_q[b]:cu_q[b + 1]], k[cu_k[b]:cu_k[b + 1]], v[cu_k[b]:cu_k[b + 1]],
+                     [0, cu_q[b + 1] - cu_q[b]], [0, cu_k[b + 1] - cu_k[b]], scale)
+        assert same(F, ob, o[cu_q[b]:cu_q[b + 1]]) and same(F, lb, l[cu_q[b]:cu_q[b + 1]])
     # row subset and thread count do not change values
     rows = [19, 0, 7, 12]
-    orow, lrow = run(q, k, v, cu_q, cu_k, scale, rows=rows, library=library, threads=1)
-    assert np.array_equal(orow, o[rows]) and np.array_equal(lrow, l[rows])
+    orow, lrow = F(q, k, v, cu_q, cu_k, scale, rows=rows, threads=1)
+    assert same(F, orow, o[rows]) and same(F, lrow, l[rows])
     # softmax rows sum to one: V = identity gives O = P
     nk = 8
     qi, ki, _ = rand_case(rng, [0, 5], [0, nk], 1, nk)
     vi = to_bf16_bits(np.eye(nk)[:, None, :])
-    oi, li = run(qi, ki, vi, [0, 5], [0, nk], 0.5, library=library)
+    oi, li = F(qi, ki, vi, [0, 5], [0, nk], 0.5)
     np.testing.assert_allclose(oi.sum(axis=-1), 1.0, rtol=0, atol=1e-14)
     assert np.all(oi >= 0)
     s = 0.5 * np.einsum("id,jd->ij", bits_to_f64(qi)[:, 0], bits_to_f64(ki)[:, 0])
     np.testing.assert_allclose(oi[:, 0], np.exp(s - li), rtol=1e-12)
     # scaling q by 2 (exact in bf16) equals doubling the scale
     qd = to_bf16_bits(2.0 * bits_to_f64(q))
-    o3, l3 = run(qd, k, v, cu_q, cu_k, scale, library=library)
-    o4, l4 = run(q, k, v, cu_q, cu_k, 2 * scale, library=library)
+    o3, l3 = F(qd, k, v, cu_q, cu_k, scale)
+    o4, l4 = F(q, k, v, cu_q, cu_k, 2 * scale)
     np.testing.assert_allclose(o3, o4, rtol=1e-13, atol=1e-15)
     np.testing.assert_allclose(l3, l4, rtol=1e-13, atol=1e-15)
 
@@ -237,15 +259,31 @@ def pin_invariants(library):
 PINS = [pin_brute_force, pin_small_integers, pin_sdpa, pin_closed_forms, pin_needle, pin_invariants]
 
 
+IMPLS = {"c": None, "blas": blas_oracle_fn}
+
+
 @pytest.fixture(scope="module")
-def default_lib():
+def built_oracle():
     oracle.build(force=False)
-    return None  # None selects the default build
 
 
+@pytest.mark.parametrize("impl", sorted(IMPLS))
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
-def test_oracle_pin(pin, default_lib):
-    pin(default_lib)
+def test_oracle_pin(pin, impl, built_oracle):
+    pin(c_oracle() if impl == "c" else IMPLS[impl])
+
+
+def test_c_and_blas_oracles_agree():
+    rng = np.random.default_rng(9)
+    cu_q, cu_k, H, D = [0, 130, 131, 400], [0, 257, 300, 300], 3, 96
+    q, k, v = rand_case(rng, cu_q, cu_k, H, D, std=1.0)
+    rows = [0, 5, 129, 130, 131, 399, 250]
+    o1, l1 = c_oracle()(q, k, v, cu_q, cu_k, 0.1, rows=rows)
+    o2, l2 = blas_oracle_fn(q, k, v, cu_q, cu_k, 0.1, rows=rows)
+    np.testing.assert_allclose(o1, o2, rtol=1e-11, atol=1e-13)
+    fin = np.isfinite(l1)
+    assert np.array_equal(fin, np.isfinite(l2)) and np.all(l2[~fin] == -np.inf)
+    np.testing.assert_allclose(l1[fin], l2[fin], rtol=1e-12, atol=1e-13)
 
 
 def test_oracle_rejects_bad_arguments():
@@ -291,12 +329,12 @@ def _build_mutant(tmp_path: Path, name: str) -> Path:
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc needed to build mutants")
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(tmp_path, name):
-    lib = oracle.load_library(_build_mutant(tmp_path, name))
+    F = c_oracle(oracle.load_library(_build_mutant(tmp_path, name)))
     failed = []
     for pin in PINS:
         try:
             with np.errstate(all="ignore"):
-                pin(lib)
+                pin(F)
         except (AssertionError, ValueError, FloatingPointError):
             failed.append(pin.__name__)
     assert failed, f"planted mistake {name} passed every pin"

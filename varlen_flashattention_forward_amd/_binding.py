@@ -1,0 +1,215 @@
+"""ctypes binding of libattn_varlen.so (include/attn_varlen.h).
+
+Argument marshalling only: tensors become device pointers, strides and token
+extents; the stream is torch's current stream. Every step of the computation
+runs in the library's HIP kernels. If the library is missing this module
+raises instead of computing anything another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from pathlib import Path
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libattn_varlen.so"
+
+OK = 0
+ENULL, EINVAL, EUNSUPPORTED, EALIGN, ECU, EMAXSEQ, EHIP = -1, -2, -3, -4, -5, -6, -7
+ERROR_NAMES = {ENULL: "ENULL", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EALIGN: "EALIGN",
+               ECU: "ECU", EMAXSEQ: "EMAXSEQ", EHIP: "EHIP"}
+
+#: every symbol include/attn_varlen.h declares
+EXPORTED_SYMBOLS = (
+    "attn_varlen_fwd", "attn_varlen_fwd_hostcu", "attn_varlen_validate", "attn_varlen_block_m",
+    "attn_varlen_count_tiles", "attn_varlen_grid_plan", "attn_varlen_segments_per_launch",
+    "attn_varlen_decode_tile", "attn_varlen_element_offset", "attn_varlen_last_error",
+)
+
+
+class AttnVarlenError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERROR_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "q_row", "q_head", "k_row", "k_head", "v_row", "v_head", "o_row", "o_head",
+        "lse_head", "q_tokens", "k_tokens")]
+
+
+_lib = None
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+
+
+def lib():
+    """Load libattn_varlen.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m varlen_flashattention_forward_amd.build` "
+                "(there is no fallback implementation)")
+        L = ctypes.CDLL(str(LIB_PATH))
+        fwd_args = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                    ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Layout), ctypes.c_float, _vp, _vp, _vp]
+        for name in ("attn_varlen_fwd", "attn_varlen_fwd_hostcu"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int32
+            f.argtypes = fwd_args
+        L.attn_varlen_validate.restype = ctypes.c_int32
+        L.attn_varlen_validate.argtypes = fwd_args[:-1]
+        L.attn_varlen_block_m.restype = ctypes.c_int32
+        L.attn_varlen_block_m.argtypes = [ctypes.c_int32]
+        L.attn_varlen_count_tiles.restype = ctypes.c_int64
+        L.attn_varlen_count_tiles.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+        L.attn_varlen_grid_plan.restype = ctypes.c_int32
+        L.attn_varlen_grid_plan.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _i64p, _i64p]
+        L.attn_varlen_segments_per_launch.restype = ctypes.c_int32
+        L.attn_varlen_segments_per_launch.argtypes = []
+        L.attn_varlen_decode_tile.restype = ctypes.c_int32
+        L.attn_varlen_decode_tile.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int64, _i32p, _i32p, _i32p]
+        L.attn_varlen_element_offset.restype = ctypes.c_int64
+        L.attn_varlen_element_offset.argtypes = [ctypes.c_int64] * 4
+        L.attn_varlen_last_error.restype = ctypes.c_char_p
+        L.attn_varlen_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().attn_varlen_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != OK:
+        raise AttnVarlenError(rc, last_error())
+
+
+def _cu_array(cu):
+    vals = [int(x) for x in cu]
+    return (ctypes.c_int32 * max(1, len(vals)))(*vals), len(vals) - 1
+
+
+# ---- host-only helpers (no GPU needed) -------------------------------------------------
+
+def block_m(head_dim: int) -> int:
+    r = lib().attn_varlen_block_m(head_dim)
+    _check(min(r, 0))
+    return r
+
+
+def count_tiles(cu_q, num_heads: int, block_m_: int) -> int:
+    arr, B = _cu_array(cu_q)
+    r = lib().attn_varlen_count_tiles(arr, B, num_heads, block_m_)
+    if r < 0:
+        _check(int(r))
+    return int(r)
+
+
+def grid_plan(cu_q, num_heads: int, head_dim: int):
+    arr, B = _cu_array(cu_q)
+    nl, nw = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().attn_varlen_grid_plan(arr, B, num_heads, head_dim, ctypes.byref(nl), ctypes.byref(nw)))
+    return nl.value, nw.value
+
+
+def segments_per_launch() -> int:
+    return lib().attn_varlen_segments_per_launch()
+
+
+def decode_tile(cu_q, num_heads: int, block_m_: int, wg: int):
+    arr, B = _cu_array(cu_q)
+    s, m, h = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().attn_varlen_decode_tile(arr, B, num_heads, block_m_, wg, ctypes.byref(s), ctypes.byref(m),
+                                         ctypes.byref(h)))
+    return s.value, m.value, h.value
+
+
+def element_offset(row: int, row_stride: int, head: int, head_stride: int) -> int:
+    return lib().attn_varlen_element_offset(row, row_stride, head, head_stride)
+
+
+def validate(q_ptr, k_ptr, v_ptr, cu_q, cu_k, num_heads, head_dim, max_q, max_k, layout: Layout,
+             scale: float, out_ptr, lse_ptr) -> int:
+    """Return code of the host-side argument check (no HIP call)."""
+    cq, B = _cu_array(cu_q)
+    ck, Bk = _cu_array(cu_k)
+    if Bk != B:
+        raise ValueError("cu_q and cu_k differ in length")
+    return lib().attn_varlen_validate(q_ptr, k_ptr, v_ptr, cq, ck, B, num_heads, head_dim, max_q,
+                                      max_k, ctypes.byref(layout), scale, out_ptr, lse_ptr)
+
+
+# ---- torch front end ----------------------------------------------------------------
+
+def _layout_of(q, k, v, out, lse, lse_head):
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{name} must be [tokens, H, D] with a contiguous D dimension")
+    return Layout(q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+                  out.stride(0), out.stride(1), lse_head, q.shape[0], k.shape[0])
+
+
+def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    softmax_scale: float | None = None, out=None, lse=None, return_lse: bool = True,
+                    cu_seqlens_q_host=None, cu_seqlens_k_host=None, stream=None):
+    """Varlen attention forward on torch's current stream.
+
+    q: [total_q, H, D], k/v: [total_k, H, D] bf16 CUDA tensors (any token and
+    head strides, contiguous D). cu_seqlens_q/k: int32 CUDA tensors [B+1].
+    When host copies of cu_seqlens are given, the synchronisation-free entry
+    point is used. Returns (out [total_q, H, D] bf16, lse [H, total_q] fp32 or None).
+    """
+    import torch
+
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    total_q, H, D = q.shape
+    if k.shape[1:] != (H, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [total_k, H, D] matching q's H and D")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((total_q, H, D), dtype=torch.bfloat16, device=q.device)
+    elif out.dtype != torch.bfloat16 or out.shape != q.shape:
+        raise ValueError("out must be bf16 with q's shape")
+    lse_head = 0
+    if lse is None and return_lse:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        if lse.dtype != torch.float32 or lse.dim() != 2 or lse.shape[0] != H or lse.stride(1) != 1 \
+                or lse.shape[1] < total_q:
+            raise ValueError("lse must be fp32 [H, >= total_q] with unit inner stride")
+        lse_head = lse.stride(0)
+    layout = _layout_of(q, k, v, out, lse, lse_head)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    L = lib()
+    lse_ptr = lse.data_ptr() if lse is not None else None
+    if cu_seqlens_q_host is not None or cu_seqlens_k_host is not None:
+        cq, B = _cu_array(cu_seqlens_q_host)
+        ck, Bk = _cu_array(cu_seqlens_k_host)
+        if B != Bk:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+        rc = L.attn_varlen_fwd_hostcu(q.data_ptr(), k.data_ptr(), v.data_ptr(), cq, ck, B, H, D,
+                                      int(max_seqlen_q), int(max_seqlen_k), ctypes.byref(layout),
+                                      float(softmax_scale), out.data_ptr(), lse_ptr, stream)
+    else:
+        for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+            if cu.dtype != torch.int32 or not cu.is_cuda or cu.dim() != 1 or not cu.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous int32 device tensor")
+        B = cu_seqlens_q.numel() - 1
+        if cu_seqlens_k.numel() != B + 1:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+        rc = L.attn_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
+                               cu_seqlens_k.data_ptr(), B, H, D, int(max_seqlen_q), int(max_seqlen_k),
+                               ctypes.byref(layout), float(softmax_scale), out.data_ptr(), lse_ptr, stream)
+    _check(rc)
+    return out, lse

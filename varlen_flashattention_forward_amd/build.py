@@ -1,0 +1,67 @@
+"""Build libattn_varlen.so (gfx950) in-tree with hipcc.
+
+    python -m varlen_flashattention_forward_amd.build
+
+Each HIP source is compiled to an object in parallel, then linked into
+varlen_flashattention_forward_amd/libattn_varlen.so. Packed FP32 VALU ops are
+disabled for the device code (-packed-fp32-ops).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+CSRC = PKG / "csrc"
+ROOT = PKG.parent
+LIB = PKG / "libattn_varlen.so"
+BUILD_DIR = PKG / "_build"
+SOURCES = ["avf_api.hip", "avf_kernel.hip"]
+ARCH = os.environ.get("AVF_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and Path(cand).exists():
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libattn_varlen.so)")
+
+
+def common_flags() -> list:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+            f"-I{ROOT / 'include'}", f"-I{CSRC}",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _compile(src: str) -> Path:
+    obj = BUILD_DIR / (Path(src).stem + ".o")
+    cmd = [hipcc(), "-c", str(CSRC / src), "-o", str(obj)] + common_flags()
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed on {src}")
+    return obj
+
+
+def build(verbose: bool = False) -> Path:
+    BUILD_DIR.mkdir(exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB.with_suffix(".so.tmp")
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", str(tmp)] + [str(o) for o in objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("linking libattn_varlen.so failed")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,328 @@
+// C ABI of the packed variable-length attention forward: argument checks,
+// the exact tile plan, and the launches. Declarations and contracts are in
+// include/attn_varlen.h.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <climits>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/attn_varlen.h"
+#include "avf_plan.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// (extent, stride) pairs of a tensor whose innermost dimension is D with
+// stride 1: true if no two elements share an address (each stride, in
+// increasing order, spans everything below it).
+bool non_overlapping(int64_t rows, int64_t row_stride, int64_t heads, int64_t head_stride,
+                     int64_t d) {
+    struct Dim { int64_t extent, stride; };
+    std::vector<Dim> dims;
+    dims.push_back({d, 1});
+    if (rows > 1) dims.push_back({rows, row_stride});
+    if (heads > 1) dims.push_back({heads, head_stride});
+    std::sort(dims.begin(), dims.end(), [](const Dim& x, const Dim& y) { return x.stride < y.stride; });
+    for (size_t i = 1; i < dims.size(); ++i) {
+        const __int128 span = (__int128)dims[i - 1].extent * dims[i - 1].stride;
+        if ((__int128)dims[i].stride < span) return false;
+    }
+    return true;
+}
+
+int32_t check_scalars(const void* q, const void* k, const void* v, int32_t B, int32_t H,
+                      int32_t D, int32_t max_q, int32_t max_k, const attn_varlen_layout* st,
+                      float scale, const void* out, const float* lse) {
+    if (B < 0) return fail(ATTN_VARLEN_EINVAL, "num_segments must be >= 0 (got %d)", B);
+    if (H <= 0) return fail(ATTN_VARLEN_EINVAL, "num_heads must be >= 1 (got %d)", H);
+    if (max_q < 0 || max_k < 0)
+        return fail(ATTN_VARLEN_EINVAL, "max_seqlen_q/k must be >= 0 (got %d, %d)", max_q, max_k);
+    if (!st) return fail(ATTN_VARLEN_ENULL, "layout is NULL");
+    if (st->q_tokens < 0 || st->k_tokens < 0 || st->q_tokens > INT32_MAX || st->k_tokens > INT32_MAX)
+        return fail(ATTN_VARLEN_EINVAL, "q_tokens/k_tokens must be in [0, 2^31) (got %lld, %lld)",
+                    (long long)st->q_tokens, (long long)st->k_tokens);
+    if (avf_block_m(D) <= 0)
+        return fail(ATTN_VARLEN_EUNSUPPORTED, "head_dim %d not supported (64, 96 or 128)", D);
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(ATTN_VARLEN_EINVAL, "softmax_scale must be finite and > 0 (got %g)", (double)scale);
+    if (B == 0) return ATTN_VARLEN_OK;
+    // tensors with no token rows may be NULL (nothing is read from or written to them)
+    if (st->q_tokens > 0 && (!q || !out)) return fail(ATTN_VARLEN_ENULL, "q and out must be non-NULL");
+    if (st->k_tokens > 0 && (!k || !v)) return fail(ATTN_VARLEN_ENULL, "k and v must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(ATTN_VARLEN_EALIGN, "q, k, v and out must be 16-byte aligned");
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return fail(ATTN_VARLEN_EALIGN, "lse must be 4-byte aligned");
+    const int64_t rows[4] = {st->q_row, st->k_row, st->v_row, st->o_row};
+    const int64_t heads[4] = {st->q_head, st->k_head, st->v_head, st->o_head};
+    const char* names = "qkvo";
+    for (int i = 0; i < 4; ++i) {
+        if (rows[i] < 1 || heads[i] < 0)
+            return fail(ATTN_VARLEN_EINVAL, "%c strides must be row >= 1, head >= 0 (got %lld, %lld)",
+                        names[i], (long long)rows[i], (long long)heads[i]);
+        if ((rows[i] & 7) || (heads[i] & 7))
+            return fail(ATTN_VARLEN_EALIGN, "%c strides must be multiples of 8 elements (got %lld, %lld)",
+                        names[i], (long long)rows[i], (long long)heads[i]);
+        if (rows[i] > ATTN_VARLEN_MAX_ROW_STRIDE)
+            return fail(ATTN_VARLEN_EUNSUPPORTED, "%c row stride %lld exceeds the limit %lld", names[i],
+                        (long long)rows[i], (long long)ATTN_VARLEN_MAX_ROW_STRIDE);
+    }
+    if (lse && st->lse_head < 0) return fail(ATTN_VARLEN_EINVAL, "lse_head must be >= 0");
+    return ATTN_VARLEN_OK;
+}
+
+int32_t check_cu(const int32_t* cu_q, const int32_t* cu_k, int32_t B, int32_t max_q,
+                 int32_t max_k, const attn_varlen_layout* st) {
+    if (!cu_q || !cu_k) return fail(ATTN_VARLEN_ENULL, "cu_seqlens_q/k must be non-NULL");
+    if (cu_q[0] != 0 || cu_k[0] != 0)
+        return fail(ATTN_VARLEN_ECU, "cu_seqlens must start at 0 (got %d, %d)", cu_q[0], cu_k[0]);
+    for (int32_t b = 0; b < B; ++b) {
+        const int64_t lq = (int64_t)cu_q[b + 1] - cu_q[b];
+        const int64_t lk = (int64_t)cu_k[b + 1] - cu_k[b];
+        if (lq < 0 || lk < 0)
+            return fail(ATTN_VARLEN_ECU, "cu_seqlens decrease at segment %d (q %lld, k %lld)", b,
+                        (long long)lq, (long long)lk);
+        if (lq > max_q || lk > max_k)
+            return fail(ATTN_VARLEN_EMAXSEQ,
+                        "segment %d has %lld query / %lld key rows, over max_seqlen %d / %d", b,
+                        (long long)lq, (long long)lk, max_q, max_k);
+    }
+    if (cu_q[B] > st->q_tokens || cu_k[B] > st->k_tokens)
+        return fail(ATTN_VARLEN_ECU, "cu_seqlens end at %d / %d tokens, past q_tokens %lld / k_tokens %lld",
+                    cu_q[B], cu_k[B], (long long)st->q_tokens, (long long)st->k_tokens);
+    return ATTN_VARLEN_OK;
+}
+
+// Checks that need the cu values: output overlap and the LSE head stride.
+int32_t check_with_cu(const int32_t* cu_q, int32_t B, int32_t H, int32_t D,
+                      const attn_varlen_layout* st, const float* lse) {
+    const int64_t total_q = cu_q[B];
+    if (!non_overlapping(total_q, st->o_row, H, st->o_head, D))
+        return fail(ATTN_VARLEN_EINVAL, "out strides (row %lld, head %lld) make elements overlap",
+                    (long long)st->o_row, (long long)st->o_head);
+    if (lse && H > 1) {
+        const int64_t lh = st->lse_head ? st->lse_head : st->q_tokens;
+        if (lh < total_q)
+            return fail(ATTN_VARLEN_EINVAL, "lse_head %lld is smaller than total_q %lld", (long long)lh,
+                        (long long)total_q);
+    }
+    return ATTN_VARLEN_OK;
+}
+
+int32_t validate_all(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                     const int32_t* cu_k, int32_t B, int32_t H, int32_t D, int32_t max_q,
+                     int32_t max_k, const attn_varlen_layout* st, float scale, const void* out,
+                     const float* lse) {
+    int32_t rc = check_scalars(q, k, v, B, H, D, max_q, max_k, st, scale, out, lse);
+    if (rc != ATTN_VARLEN_OK || B == 0) return rc;
+    rc = check_cu(cu_q, cu_k, B, max_q, max_k, st);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    return check_with_cu(cu_q, B, H, D, st, lse);
+}
+
+// Exact tile count of segments [b0, b1).
+int64_t tiles_of(const int32_t* cu_q, int32_t b0, int32_t b1, int32_t H, int32_t bm) {
+    int64_t t = 0;
+    for (int32_t b = b0; b < b1; ++b) {
+        const int64_t lq = (int64_t)cu_q[b + 1] - cu_q[b];
+        t += (lq + bm - 1) / bm;
+    }
+    return t * H;
+}
+
+// Fill the launch plan for segments [b0, b1); returns the tile count.
+int64_t fill_plan(AvfLaunchArgs& a, const int32_t* cu_q, const int32_t* cu_k, int32_t b0,
+                  int32_t b1, int32_t H, int32_t bm) {
+    int64_t t = 0;
+    a.num_segs = b1 - b0;
+    for (int32_t s = 0; s <= b1 - b0; ++s) {
+        a.tile_start[s] = (int32_t)t;
+        a.q_start[s] = cu_q[b0 + s];
+        a.k_start[s] = cu_k[b0 + s];
+        if (s < b1 - b0) {
+            const int64_t lq = (int64_t)cu_q[b0 + s + 1] - cu_q[b0 + s];
+            t += H * ((lq + bm - 1) / bm);
+        }
+    }
+    a.num_tiles = (int32_t)t;
+    return t;
+}
+
+// Largest tile count one launch may have: grid size in work-items must stay
+// below 2^32 (HSA dispatch limit) with 256 threads per workgroup.
+constexpr int64_t kMaxTilesPerLaunch = (int64_t)1 << 23;
+
+int32_t run(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
+            int32_t B, int32_t H, int32_t D, const attn_varlen_layout* st, float scale, void* out,
+            float* lse, hipStream_t stream) {
+    const int32_t bm = avf_block_m(D);
+    AvfLaunchArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q; a.k = k; a.v = v; a.o = out; a.lse = lse;
+    a.q_row = st->q_row; a.q_head = st->q_head;
+    a.k_row = st->k_row; a.k_head = st->k_head;
+    a.v_row = st->v_row; a.v_head = st->v_head;
+    a.o_row = st->o_row; a.o_head = st->o_head;
+    a.lse_head = st->lse_head ? st->lse_head : st->q_tokens;
+    a.scale = scale;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    a.num_heads = H;
+    for (int32_t b0 = 0; b0 < B;) {
+        // segments of this launch: at most AVF_SEGS_PER_LAUNCH and at most kMaxTilesPerLaunch tiles
+        int32_t b1 = b0;
+        int64_t t = 0;
+        while (b1 < B && b1 - b0 < AVF_SEGS_PER_LAUNCH) {
+            const int64_t tb = tiles_of(cu_q, b1, b1 + 1, H, bm);
+            if (t + tb > kMaxTilesPerLaunch && b1 > b0) break;
+            if (tb > kMaxTilesPerLaunch)
+                return fail(ATTN_VARLEN_EUNSUPPORTED, "segment %d needs %lld tiles (limit %lld per launch)",
+                            b1, (long long)tb, (long long)kMaxTilesPerLaunch);
+            t += tb;
+            ++b1;
+        }
+        const int64_t tiles = fill_plan(a, cu_q, cu_k, b0, b1, H, bm);
+        if (tiles > 0) {
+            const hipError_t e = avf_launch(a, D, stream);
+            if (e != hipSuccess)
+                return fail(ATTN_VARLEN_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+        }
+        b0 = b1;
+    }
+    return ATTN_VARLEN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t attn_varlen_validate(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                             const int32_t* cu_k, int32_t B, int32_t H, int32_t D, int32_t max_q,
+                             int32_t max_k, const attn_varlen_layout* st, float scale,
+                             const void* out, const float* lse) {
+    g_last_error.clear();
+    return validate_all(q, k, v, cu_q, cu_k, B, H, D, max_q, max_k, st, scale, out, lse);
+}
+
+int32_t attn_varlen_fwd_hostcu(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                               const int32_t* cu_k, int32_t B, int32_t H, int32_t D, int32_t max_q,
+                               int32_t max_k, const attn_varlen_layout* st, float scale, void* out,
+                               float* lse, void* stream) {
+    g_last_error.clear();
+    const int32_t rc = validate_all(q, k, v, cu_q, cu_k, B, H, D, max_q, max_k, st, scale, out, lse);
+    if (rc != ATTN_VARLEN_OK || B == 0) return rc;
+    return run(q, k, v, cu_q, cu_k, B, H, D, st, scale, out, lse, static_cast<hipStream_t>(stream));
+}
+
+int32_t attn_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_q_dev,
+                        const int32_t* cu_k_dev, int32_t B, int32_t H, int32_t D, int32_t max_q,
+                        int32_t max_k, const attn_varlen_layout* st, float scale, void* out,
+                        float* lse, void* stream) {
+    g_last_error.clear();
+    int32_t rc = check_scalars(q, k, v, B, H, D, max_q, max_k, st, scale, out, lse);
+    if (rc != ATTN_VARLEN_OK || B == 0) return rc;
+    if (!cu_q_dev || !cu_k_dev) return fail(ATTN_VARLEN_ENULL, "cu_seqlens_q/k must be non-NULL");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    std::vector<int32_t> cu((size_t)2 * (B + 1));
+    hipError_t e = hipMemcpyAsync(cu.data(), cu_q_dev, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(cu.data() + B + 1, cu_k_dev, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "reading cu_seqlens failed: %s", hipGetErrorString(e));
+    const int32_t* cq = cu.data();
+    const int32_t* ck = cu.data() + B + 1;
+    rc = check_cu(cq, ck, B, max_q, max_k, st);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    rc = check_with_cu(cq, B, H, D, st, lse);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    return run(q, k, v, cq, ck, B, H, D, st, scale, out, lse, s);
+}
+
+int32_t attn_varlen_block_m(int32_t head_dim) {
+    const int32_t bm = avf_block_m(head_dim);
+    return bm > 0 ? bm : ATTN_VARLEN_EUNSUPPORTED;
+}
+
+int64_t attn_varlen_count_tiles(const int32_t* cu_q, int32_t B, int32_t H, int32_t block_m) {
+    g_last_error.clear();
+    if (!cu_q) return fail(ATTN_VARLEN_ENULL, "cu_seqlens_q is NULL");
+    if (B < 0 || H <= 0 || block_m <= 0) return fail(ATTN_VARLEN_EINVAL, "bad counts");
+    if (B > 0 && cu_q[0] != 0) return fail(ATTN_VARLEN_ECU, "cu_seqlens_q must start at 0");
+    for (int32_t b = 0; b < B; ++b)
+        if (cu_q[b + 1] < cu_q[b]) return fail(ATTN_VARLEN_ECU, "cu_seqlens_q decreases at %d", b);
+    return tiles_of(cu_q, 0, B, H, block_m);
+}
+
+int32_t attn_varlen_segments_per_launch(void) { return AVF_SEGS_PER_LAUNCH; }
+
+int32_t attn_varlen_grid_plan(const int32_t* cu_q, int32_t B, int32_t H, int32_t D,
+                              int64_t* launches, int64_t* workgroups) {
+    g_last_error.clear();
+    if (!cu_q || !launches || !workgroups) return fail(ATTN_VARLEN_ENULL, "NULL argument");
+    const int32_t bm = avf_block_m(D);
+    if (bm <= 0) return fail(ATTN_VARLEN_EUNSUPPORTED, "head_dim %d not supported", D);
+    if (B < 0 || H <= 0) return fail(ATTN_VARLEN_EINVAL, "bad counts");
+    int64_t nl = 0, nw = 0;
+    for (int32_t b0 = 0; b0 < B;) {
+        int32_t b1 = b0;
+        int64_t t = 0;
+        while (b1 < B && b1 - b0 < AVF_SEGS_PER_LAUNCH) {
+            const int64_t tb = tiles_of(cu_q, b1, b1 + 1, H, bm);
+            if (t + tb > kMaxTilesPerLaunch && b1 > b0) break;
+            t += tb;
+            ++b1;
+        }
+        if (t > 0) ++nl;
+        nw += t;
+        b0 = b1;
+    }
+    *launches = nl;
+    *workgroups = nw;
+    return ATTN_VARLEN_OK;
+}
+
+int32_t attn_varlen_decode_tile(const int32_t* cu_q, int32_t B, int32_t H, int32_t block_m,
+                                int64_t wg, int32_t* segment, int32_t* q_block, int32_t* head) {
+    g_last_error.clear();
+    if (!cu_q || !segment || !q_block || !head) return fail(ATTN_VARLEN_ENULL, "NULL argument");
+    if (B <= 0 || B > AVF_SEGS_PER_LAUNCH || H <= 0 || block_m <= 0)
+        return fail(ATTN_VARLEN_EINVAL, "bad counts");
+    AvfLaunchArgs a;
+    std::memset(&a, 0, sizeof a);
+    const int64_t t = fill_plan(a, cu_q, cu_q, 0, B, H, block_m);
+    if (wg < 0 || wg >= t) return fail(ATTN_VARLEN_EINVAL, "workgroup %lld outside grid of %lld", (long long)wg, (long long)t);
+    const int32_t lin = avf_linear_tile((int32_t)wg, a.num_tiles);
+    const AvfTile tile = avf_decode(lin, a.tile_start, a.q_start, a.num_segs, H, block_m);
+    *segment = tile.seg;
+    *q_block = tile.mblk;
+    *head = tile.head;
+    return ATTN_VARLEN_OK;
+}
+
+int64_t attn_varlen_element_offset(int64_t row, int64_t row_stride, int64_t head,
+                                   int64_t head_stride) {
+    return avf_elem_offset(row, row_stride, head, head_stride);
+}
+
+const char* attn_varlen_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Launch arguments and the tile map shared by the host planner and the gfx950
+// kernel (both sides of the library; nothing here is used by anything else).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// Segments handled by one launch. The plan of a launch (tile prefix and
+// segment starts) travels in the kernel arguments, so no device workspace is
+// needed; longer segment lists are split over several launches.
+#define AVF_SEGS_PER_LAUNCH 128
+
+// Chiplets (XCDs) of an MI355X. Workgroups are handed to XCDs round-robin in
+// dispatch order; the tile map below gives each XCD a contiguous run of tiles
+// so the workgroups sharing one XCD's L2 walk the same (segment, head) K/V.
+#define AVF_NUM_XCD 8
+
+struct AvfLaunchArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    // element strides (int64: offsets are formed in 64-bit arithmetic)
+    int64_t q_row, q_head, k_row, k_head, v_row, v_head, o_row, o_head, lse_head;
+    float scale_log2e;  // softmax_scale * log2(e): logits in base-2 units
+    float scale;        // softmax_scale: the LSE is reported in natural-log units
+    int32_t num_heads;
+    int32_t num_segs;   // segments in this launch (1..AVF_SEGS_PER_LAUNCH)
+    int32_t num_tiles;  // == gridDim.x, exact
+    // tile_start[s] = num_heads * sum_{s' < s} ceil(Lq_s' / BM); tile_start[num_segs] = num_tiles
+    int32_t tile_start[AVF_SEGS_PER_LAUNCH + 1];
+    // cu_seqlens entries of this launch's segments, absolute token indices
+    int32_t q_start[AVF_SEGS_PER_LAUNCH + 1];
+    int32_t k_start[AVF_SEGS_PER_LAUNCH + 1];
+};
+
+struct AvfTile {
+    int32_t seg, mblk, head;
+};
+
+// Workgroup index -> linear tile index. Linear tiles are ordered (segment,
+// head, query block) with the query block fastest. Workgroup w runs on XCD
+// w % 8 as its (w / 8)-th workgroup; XCD x owns the contiguous linear range
+// [x*q + min(x, r), ...) of length q + (x < r) where T = 8q + r. This is a
+// bijection of [0, T) for every T >= 1.
+__host__ __device__ inline int32_t avf_linear_tile(int32_t wg, int32_t num_tiles) {
+    const int32_t q = num_tiles / AVF_NUM_XCD;
+    const int32_t r = num_tiles % AVF_NUM_XCD;
+    const int32_t x = wg % AVF_NUM_XCD;
+    const int32_t s = wg / AVF_NUM_XCD;
+    return x * q + (x < r ? x : r) + s;
+}
+
+// Linear tile -> (segment, query block, head). `tile_start` is the launch's
+// prefix array; empty segments have tile_start[s] == tile_start[s+1] and are
+// never returned (the largest s with tile_start[s] <= L owns L).
+template <typename Starts>
+__host__ __device__ inline AvfTile avf_decode(int32_t linear, const Starts& tile_start,
+                                              const Starts& q_start, int32_t num_segs,
+                                              int32_t num_heads, int32_t block_m) {
+    int32_t lo = 0, hi = num_segs - 1;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (tile_start[mid] <= linear)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const int32_t lq = q_start[lo + 1] - q_start[lo];
+    const int32_t mtiles = (lq + block_m - 1) / block_m;
+    const int32_t r = linear - tile_start[lo];
+    AvfTile t;
+    t.seg = lo;
+    t.head = r / mtiles;
+    t.mblk = r - t.head * mtiles;
+    (void)num_heads;
+    return t;
+}
+
+__host__ __device__ inline int64_t avf_elem_offset(int64_t row, int64_t row_stride, int64_t head,
+                                                   int64_t head_stride) {
+    return row * row_stride + head * head_stride;
+}
+
+// Host-side launcher implemented next to the kernels.
+hipError_t avf_launch(const AvfLaunchArgs& args, int32_t head_dim, hipStream_t stream);
+int32_t avf_block_m(int32_t head_dim);
