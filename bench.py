@@ -81,8 +81,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense_77k")
-    ap.add_argument("--cpu-rows", type=int, default=8, help="query rows per segment for the CPU baseline")
+    ap.add_argument("--cpu-rows", type=int, default=48, help="query rows per segment for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library runs on a single MI355X and has no "
@@ -94,9 +96,18 @@ def main() -> int:
     import varlen_flashattention_forward_amd as avf
     from varlen_flashattention_forward_amd.workloads import WORKLOADS, make_inputs
 
-    w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {n} bytes 3 times")
+        return 0
+    w = WORKLOADS[args.workload]
     avf.lib()
     log(f"[bench] workload {w.name}: H={w.num_heads} D={w.head_dim} segments={w.num_segments} "
         f"total_q={w.total_q} total_k={w.total_k}")

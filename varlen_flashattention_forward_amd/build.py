@@ -18,8 +18,8 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 ROOT = PKG.parent
-LIB = PKG / "libattn_varlen.so"
-BUILD_DIR = PKG / "_build"
+LIB = Path(os.environ.get("AVF_LIB_OUT", PKG / "libattn_varlen.so"))
+BUILD_DIR = Path(os.environ.get("AVF_BUILD_DIR", PKG / "_build"))
 SOURCES = ["avf_api.hip", "avf_kernel.hip"]
 ARCH = os.environ.get("AVF_OFFLOAD_ARCH", "gfx950")
 
@@ -34,7 +34,15 @@ def hipcc() -> str:
 def common_flags() -> list:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
             f"-I{ROOT / 'include'}", f"-I{CSRC}",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in architectural VGPRs, so the softmax rescale
+            # and epilogue touch them without AGPR<->VGPR copies
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1"] + extra_flags()
+
+
+def extra_flags() -> list:
+    """Additional hipcc flags from AVF_EXTRA_FLAGS (tuning builds)."""
+    return os.environ.get("AVF_EXTRA_FLAGS", "").split()
 
 
 def _compile(src: str) -> Path:
@@ -48,7 +56,7 @@ def _compile(src: str) -> Path:
 
 
 def build(verbose: bool = False) -> Path:
-    BUILD_DIR.mkdir(exist_ok=True)
+    BUILD_DIR.mkdir(parents=True, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB.with_suffix(".so.tmp")

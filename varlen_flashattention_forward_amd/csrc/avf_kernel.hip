@@ -43,6 +43,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
+// Largest per-lane partial row sum of softmax weights accepted before the
+// reference max is moved (bounds every weight by 2^16).
+constexpr float kPsumMax = 65536.0f;
+
 // gfx9 raw buffer descriptor word 3: 32-bit data format, no swizzle, no
 // index stride; records are bytes and out-of-range loads return 0.
 constexpr int kBufWord3 = 0x00020000;
@@ -121,10 +125,11 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
         for (int db = 0; db < T::DB; ++db)
 #pragma unroll
             for (int e = 0; e < 16; ++e) o[qb][db][e] = 0.f;
-    float m_i[QB], l_i[QB];
+    float m_i[QB], mc_i[QB], l_i[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         m_i[qb] = -INFINITY;
+        mc_i[qb] = -INFINITY;
         l_i[qb] = 0.f;
     }
     const float c = a.scale_log2e;
@@ -198,6 +203,10 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
         store_tile(0);
     }
     __syncthreads();
+    // Every global load issued so far (Q fragments, first K/V tile) is complete
+    // here; saying so keeps the compiler's wait counters inside the loop from
+    // holding the MFMAs until the next tile's prefetch has landed.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
 
     for (int32_t j = 0; j < nkt; ++j) {
         const int buf = j & 1;
@@ -216,13 +225,15 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) s[qb][e] = 0.f;
+            bf16x8 ka[T::KS];
 #pragma unroll
-            for (int ks = 0; ks < T::KS; ++ks) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + (kb * 32 + l32) * T::KP + (ks * 16 + hf * 8) * 2);
+            for (int ks = 0; ks < T::KS; ++ks)
+                ka[ks] = *reinterpret_cast<const bf16x8*>(kl + (kb * 32 + l32) * T::KP + (ks * 16 + hf * 8) * 2);
+#pragma unroll
+            for (int ks = 0; ks < T::KS; ++ks)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], s[qb], 0, 0, 0);
-            }
+                    s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[qb][ks], s[qb], 0, 0, 0);
             if (nk < (kb + 1) * 32) {
                 // keys past the segment end: element e holds key kb*32 + 8*(e/4) + 4*hf + e%4
 #pragma unroll
@@ -233,30 +244,53 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
                         for (int qb = 0; qb < QB; ++qb) s[qb][e] = -INFINITY;
                 }
             }
+            // Online softmax against a lazily moved reference max m_i: the
+            // weights are p = exp2(c*s - c*m_i). Every p is bounded by its row's
+            // partial sum, so while each lane's sum stays <= kPsumMax nothing
+            // can overflow and the reference may stay where it is. Otherwise
+            // (first block, m_i = -inf; or a row max that grew by more than
+            // log2(kPsumMax)) the wave takes this block's row max, rescales O and
+            // l by exp2(c*(m_old - m_new)) and recomputes p. Same softmax; the
+            // common path has neither a max reduction nor an accumulator rescale.
             bf16x8 pk[QB][2];
+            float psum[QB];
+            auto weights = [&]() {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float mx = s[qb][0];
+                for (int qb = 0; qb < QB; ++qb) {
+                    float acc = 0.f;
 #pragma unroll
-                for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[qb][e]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float mnew = fmaxf(m_i[qb], mx);
-                const float alpha = __builtin_amdgcn_exp2f((m_i[qb] - mnew) * c);
-                const float mc = mnew * c;
-                float psum = 0.f;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][e], c, -mc));
-                    psum += p;
-                    pk[qb][e >> 3][e & 7] = (__bf16)p;
+                    for (int e = 0; e < 16; ++e) {
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][e], c, -mc_i[qb]));
+                        acc += p;
+                        pk[qb][e >> 3][e & 7] = (__bf16)p;
+                    }
+                    psum[qb] = acc;
                 }
-                l_i[qb] = l_i[qb] * alpha + psum;
-                m_i[qb] = mnew;
+            };
+            weights();
+            bool over = false;
 #pragma unroll
-                for (int db = 0; db < T::DB; ++db)
+            for (int qb = 0; qb < QB; ++qb) over |= !(psum[qb] <= kPsumMax);  // NaN counts as over
+            if (__builtin_amdgcn_ballot_w64(over) != 0) {
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
+                for (int qb = 0; qb < QB; ++qb) {
+                    float v = s[qb][0];
+#pragma unroll
+                    for (int e = 1; e < 16; ++e) v = fmaxf(v, s[qb][e]);
+                    const float mnew = fmaxf(m_i[qb], fmaxf(v, __shfl_xor(v, 32)));
+                    const float alpha = __builtin_amdgcn_exp2f((m_i[qb] - mnew) * c);
+                    l_i[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
+                    m_i[qb] = mnew;
+                    mc_i[qb] = mnew * c;
+                }
+                weights();
             }
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) l_i[qb] += psum[qb];
             // O^T += V^T P^T over the 32 keys, two 16-key MFMA steps
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2)
@@ -308,11 +342,23 @@ hipError_t launch_cfg(const AvfLaunchArgs& a, hipStream_t stream) {
 }
 
 // Per head_dim tile configuration: (QB query blocks of 32 rows per wave,
-// NW waves, BN keys per K/V stage). BM = QB * 32 * NW.
+// NW waves, BN keys per K/V stage). BM = QB * 32 * NW. Overridable at build
+// time (-DAVF_CFG_D128=QB,NW,BN) for tuning sweeps.
+#ifndef AVF_CFG_D64
+#define AVF_CFG_D64 1, 8, 64
+#endif
+#ifndef AVF_CFG_D96
+#define AVF_CFG_D96 1, 8, 64
+#endif
+#ifndef AVF_CFG_D128
+#define AVF_CFG_D128 1, 8, 64
+#endif
+template <int QB_, int NW_, int BN_>
+struct CfgOf { static constexpr int QB = QB_, NW = NW_, BN = BN_; };
 template <int D> struct Cfg;
-template <> struct Cfg<64> { static constexpr int QB = 2, NW = 4, BN = 64; };
-template <> struct Cfg<96> { static constexpr int QB = 2, NW = 4, BN = 64; };
-template <> struct Cfg<128> { static constexpr int QB = 2, NW = 4, BN = 64; };
+template <> struct Cfg<64> : CfgOf<AVF_CFG_D64> {};
+template <> struct Cfg<96> : CfgOf<AVF_CFG_D96> {};
+template <> struct Cfg<128> : CfgOf<AVF_CFG_D128> {};
 
 template <int D>
 constexpr int block_m_of() { return Cfg<D>::QB * 32 * Cfg<D>::NW; }
