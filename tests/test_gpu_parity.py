@@ -291,3 +291,55 @@ def test_stride_threshold_pair():
         compare(og, lg, ro, rl, w.name)
         del t, o, l
         torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ softmax reference moves
+
+def _run_custom(q, k, v, cq, ck, label):
+    H, D = q.shape[1], q.shape[2]
+    w = custom(label, H, D, cq, ck)
+    t = {"q": q.to(DEV), "k": k.to(DEV), "v": v.to(DEV),
+         "cu_q": torch.tensor(cq, dtype=torch.int32, device=DEV),
+         "cu_k": torch.tensor(ck, dtype=torch.int32, device=DEV),
+         "out": torch.full((w.total_q, H, D), CANARY, dtype=torch.bfloat16, device=DEV),
+         "lse": torch.full((H, w.total_q), CANARY, dtype=torch.float32, device=DEV)}
+    o, l = run_gpu(t, w)
+    rows = list(range(w.total_q))
+    og, lg = gather(o, l, rows, w.total_q)
+    ro, rl = oracle.attn_varlen_fwd(q, k, v, cq, ck, f32(w.softmax_scale), rows=rows)
+    return compare(og, lg, ro, rl, label)
+
+
+@pytest.mark.parametrize("D", [64, 96, 128])
+def test_reference_moves_with_growing_logits(D):
+    """Logits rise along the keys by ~70 base-2 units, so the softmax reference
+    has to move several times inside segments (also while the next 32-key
+    block's scores are already formed); a second segment falls instead."""
+    announce(f"growing logits D={D}")
+    g = torch.Generator().manual_seed(D)
+    H, L, nq = 2, 700, 300
+    scale = 1.0 / math.sqrt(D)
+    c = scale * 1.4426950408889634
+    a = 8.0
+    k = torch.randn((2 * L, H, D), generator=g) * 0.3
+    ramp = torch.linspace(0.0, 70.0 / (c * a), L)
+    k[:L, :, 0] = ramp[:, None]
+    k[L:, :, 0] = ramp.flip(0)[:, None]
+    q = torch.randn((2 * nq, H, D), generator=g) * 0.3
+    q[:, :, 0] = a
+    v = torch.randn((2 * L, H, D), generator=g)
+    _run_custom(q.bfloat16(), k.bfloat16(), v.bfloat16(), [0, nq, 2 * nq], [0, L, 2 * L], f"growing_d{D}")
+
+
+def test_reference_from_first_block_when_all_logits_negative():
+    """Every logit is about -130 (base-2 units): the reference must be taken
+    from the data, or every weight would underflow to zero."""
+    announce("all-negative logits")
+    g = torch.Generator().manual_seed(1)
+    H, D, L, nq = 2, 128, 333, 77
+    u = torch.randn((H, D), generator=g)
+    u = u / u.norm(dim=-1, keepdim=True) * 32.0   # q.k ~ -1024, c*s ~ -130
+    k = u[None].repeat(L, 1, 1) + torch.randn((L, H, D), generator=g) * 0.05
+    q = -u[None].repeat(nq, 1, 1) + torch.randn((nq, H, D), generator=g) * 0.05
+    v = torch.randn((L, H, D), generator=g)
+    _run_custom(q.bfloat16(), k.bfloat16(), v.bfloat16(), [0, nq], [0, L], "all_negative")

@@ -1,8 +1,9 @@
 // Packed variable-length attention forward for gfx950 (MI355X, CDNA4).
 //
 // One workgroup computes one tile: BM query rows of one head of one segment,
-// streaming that segment's K/V in blocks of BN keys through double-buffered
-// LDS. The operation is the flash-attention varlen forward with its LSE
+// streaming that segment's K/V in stages of BN keys through double-buffered
+// LDS. K and V reach LDS by buffer loads that write LDS directly (no
+// registers, no LDS store instructions), one stage ahead of the compute. The operation is the flash-attention varlen forward with its LSE
 // (the (out, lse) return of flash_attn_varlen_func on the "[FA4] cute varlen
 // backward: int32 overflow in _bwd_preprocess ..." page); the online softmax
 // keeps a running row maximum m and sum l and rescales the accumulator when m
@@ -14,10 +15,11 @@
 //                   The 32x32 result puts ONE query row per lane pair
 //                   (lane l and l+32, 16 keys each), so the row max needs one
 //                   cross-half exchange and the row sum none until the end.
-//   O^T += V^T P^T: A = 32 dims x 16 keys of V^T (LDS), B = P^T, which is the
-//                   S^T result itself, rounded to bf16 in place: the key order
-//                   of the MFMA result is matched by storing V^T in LDS with
-//                   key bits 2 and 3 swapped inside every 16-key group.
+//   O^T += V^T P^T: A = 32 dims x 16 keys of V^T, B = P^T, which is the S^T
+//                   result itself rounded to bf16 in place. V stays row-major
+//                   in LDS; two transposing reads (ds_read_b64_tr_b16) per
+//                   MFMA deliver V^T in exactly the key order of the S^T
+//                   result, so P never leaves registers.
 //   O^T accumulates with one query row per lane pair too, so the rescale by
 //   exp2(m_old - m_new) is a per-lane scalar.
 // Offsets: every tensor base is formed in int64 (row * row_stride + head *
@@ -33,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "avf_plan.h"
 
 namespace {
@@ -42,10 +46,13 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 // Largest per-lane partial row sum of softmax weights accepted before the
 // reference max is moved (bounds every weight by 2^16).
 constexpr float kPsumMax = 65536.0f;
+
 
 // gfx9 raw buffer descriptor word 3: 32-bit data format, no swizzle, no
 // index stride; records are bytes and out-of-range loads return 0.
@@ -56,9 +63,35 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
                                              kBufWord3);
 }
 
-// Position of key k (0..BN-1) inside a V^T row in LDS: bits 2 and 3 swapped.
-__device__ constexpr int vt_pos(int k) {
-    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+// 16-byte buffer load written straight to LDS: lane l of the wave fills
+// lds[16*l, 16*l + 16) (LDS base in M0, wave-uniform) with the record at
+// `voffset`. The builtin exists only for the device pass; the host pass must
+// not see it or it silently drops the kernel's launch stub.
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16,
+                                             voffset, 0, 0, 0);
+#endif
+}
+
+// LDS rows of K and V are unpadded (2*D bytes); the 16-byte chunks of a row are
+// permuted by XOR with a function of the key so that the MFMA fragment reads
+// hit all 64 banks (256 bytes) of gfx950's LDS in every phase:
+//  K (ds_read_b128: 16 lanes per phase, 16 consecutive keys, same chunk):
+//    D = 128 (16 chunks/row): chunk ^= key % 16;
+//    D = 64 (8 chunks, rows alternate bank halves): chunk ^= (key / 2) % 8;
+//    D = 96 (12 chunks, 192 B rows cycle through 4 bank offsets): chunk ^= (key / 4) % 4.
+//  V (ds_read_b64_tr_b16: 32 lanes per phase, 4 consecutive keys x 4 chunks):
+//    D = 128: chunk ^= 4 * (key % 4); D = 64: chunk ^= 4 * ((key / 2) % 2);
+//    D = 96: none needed (the 192-byte pitch already spreads the 4 rows).
+// The XOR never leaves the row (it only flips low chunk-index bits).
+template <int D>
+__device__ constexpr int k_swz(int key) {
+    return D == 128 ? key & 15 : D == 64 ? (key >> 1) & 7 : (key >> 2) & 3;
+}
+template <int D>
+__device__ constexpr int v_swz(int key) {
+    return D == 128 ? (key & 3) << 2 : D == 64 ? ((key >> 1) & 1) << 2 : 0;
 }
 
 template <int D, int QB, int NW, int BN>
@@ -68,16 +101,12 @@ struct Tile {
     static constexpr int KS = D / 16;           // MFMA k-steps over D
     static constexpr int DB = D / 32;           // 32-wide column blocks of O
     static constexpr int KB = BN / 32;          // 32-key sub-blocks per K/V tile
-    static constexpr int KP = D * 2 + 16;       // K row pitch in LDS, bytes (padded)
-    static constexpr int VP = BN * 2 + 16;      // V^T row pitch in LDS, bytes (padded)
-    static constexpr int KBYTES = BN * KP;
-    static constexpr int VBYTES = D * VP;
-    static constexpr int STAGE = KBYTES + VBYTES;
-    static constexpr int KCH = BN * D / 8;      // 16-byte chunks per K tile
-    static constexpr int KPT = (KCH + NT - 1) / NT;
-    static constexpr int VTASK = (BN / 4) * (D / 8);  // 4 keys x 8 dims per task
-    static constexpr int VPT = (VTASK + NT - 1) / NT;
-    static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
+    static constexpr int ROWB = D * 2;          // bytes per K/V row in LDS
+    static constexpr int KBYTES = BN * ROWB;    // K part of a stage
+    static constexpr int STAGE = 2 * BN * ROWB; // K then V
+    static constexpr int NI = BN * ROWB / 1024; // 1 KiB direct loads per array and stage
+    static constexpr int NIW = (NI + NW - 1) / NW;
+    static_assert(D % 32 == 0 && BN % 32 == 0 && (BN * ROWB) % 1024 == 0, "tile shape");
 };
 
 template <int D, int QB, int NW, int BN>
@@ -125,6 +154,9 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
         for (int db = 0; db < T::DB; ++db)
 #pragma unroll
             for (int e = 0; e < 16; ++e) o[qb][db][e] = 0.f;
+    // m_i: the row's softmax reference (a row maximum of the raw scores seen
+    // at some block, -inf before the first); mc_i = m_i * c; l_i: this lane's
+    // partial row sum of weights against that reference.
     float m_i[QB], mc_i[QB], l_i[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -132,181 +164,217 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
         mc_i[qb] = -INFINITY;
         l_i[qb] = 0.f;
     }
-    const float c = a.scale_log2e;
+    const float c = a.scale_log2e;  // weights are exp2(c * (s - m))
 
-    // ---- K/V staging: global -> registers (prefetch) -> LDS ----
+    // ---- K/V staging: buffer loads straight into LDS ----
+    // Stage j covers keys [j*BN, j*BN + BN) of the segment. Each wave issues
+    // 1 KiB loads; lane l of load i fills LDS bytes [i*1024 + 16*l, +16), which
+    // is chunk `slot` of row `key` of the stage, so it fetches chunk
+    // slot ^ swz(key) of that key's row. Rows past the segment end re-read its
+    // last row (finite data; they are masked out of the softmax).
     const int32_t nkt = (lk + BN - 1) / BN;
     const uint32_t k_rs = (uint32_t)(a.k_row * 2);
     const uint32_t v_rs = (uint32_t)(a.v_row * 2);
-    i32x4 kst[T::KPT];
-    i32x4 vst[T::VPT][4];
-
-    auto load_tile = [&](int32_t j) {
+    auto load_stage = [&](int32_t j, int buf) {
         const int32_t key0 = j * BN;
         const int32_t nk = min(BN, lk - key0);
         const char* kp = (const char*)a.k + 2 * avf_elem_offset(k_tok0 + key0, a.k_row, h, a.k_head);
         const char* vp = (const char*)a.v + 2 * avf_elem_offset(k_tok0 + key0, a.v_row, h, a.v_head);
         const auto krs = make_rsrc(kp, (uint32_t)(nk - 1) * k_rs + 2 * D);
         const auto vrs = make_rsrc(vp, (uint32_t)(nk - 1) * v_rs + 2 * D);
-#pragma unroll
-        for (int cI = 0; cI < T::KPT; ++cI) {
-            const int id = tid + cI * T::NT;
-            if (T::KCH % T::NT == 0 || id < T::KCH) {
-                const int key = id / (D / 8), dc = id % (D / 8);
-                kst[cI] = __builtin_amdgcn_raw_buffer_load_b128(krs, key * k_rs + dc * 16, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int cI = 0; cI < T::VPT; ++cI) {
-            const int id = tid + cI * T::NT;
-            if (T::VTASK % T::NT == 0 || id < T::VTASK) {
-                const int kq = id % (BN / 4), dc = id / (BN / 4);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    vst[cI][r] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (4 * kq + r) * v_rs + dc * 16, 0, 0);
-            }
-        }
-    };
-
-    auto store_tile = [&](int buf) {
         char* kl = lds + buf * T::STAGE;
         char* vl = kl + T::KBYTES;
 #pragma unroll
-        for (int cI = 0; cI < T::KPT; ++cI) {
-            const int id = tid + cI * T::NT;
-            if (T::KCH % T::NT == 0 || id < T::KCH) {
-                const int key = id / (D / 8), dc = id % (D / 8);
-                *reinterpret_cast<i32x4*>(kl + key * T::KP + dc * 16) = kst[cI];
-            }
-        }
-#pragma unroll
-        for (int cI = 0; cI < T::VPT; ++cI) {
-            const int id = tid + cI * T::NT;
-            if (T::VTASK % T::NT == 0 || id < T::VTASK) {
-                const int kq = id % (BN / 4), dc = id / (BN / 4);
-                const int pos = vt_pos(4 * kq);
-#pragma unroll
-                for (int cc = 0; cc < 8; ++cc) {
-                    const int e = cc >> 1;
-                    const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-                    i32x2 w;
-                    w[0] = (int)__builtin_amdgcn_perm((uint32_t)vst[cI][1][e], (uint32_t)vst[cI][0][e], sel);
-                    w[1] = (int)__builtin_amdgcn_perm((uint32_t)vst[cI][3][e], (uint32_t)vst[cI][2][e], sel);
-                    *reinterpret_cast<i32x2*>(vl + (dc * 8 + cc) * T::VP + pos * 2) = w;
-                }
+        for (int m = 0; m < T::NIW; ++m) {
+            const int i = wave + NW * m;
+            if (T::NI % NW == 0 || i < T::NI) {
+                const int pos = i * 1024 + 16 * lane;
+                const int key = pos / T::ROWB;
+                const int slot = (pos % T::ROWB) >> 4;
+                const uint32_t kc = (uint32_t)min(key, nk - 1);
+                load_lds16(krs, kl + i * 1024, kc * k_rs + ((slot ^ k_swz<D>(key)) << 4));
+                load_lds16(vrs, vl + i * 1024, kc * v_rs + ((slot ^ v_swz<D>(key)) << 4));
             }
         }
     };
 
-    if (nkt > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
-    // Every global load issued so far (Q fragments, first K/V tile) is complete
-    // here; saying so keeps the compiler's wait counters inside the loop from
-    // holding the MFMAs until the next tile's prefetch has landed.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
-
-    for (int32_t j = 0; j < nkt; ++j) {
-        const int buf = j & 1;
-        const bool more = j + 1 < nkt;
-        if (more) load_tile(j + 1);
-        const char* kl = lds + buf * T::STAGE;
-        const char* vl = kl + T::KBYTES;
-        const int32_t nk = min(BN, lk - j * BN);
-
+    // ---- per-sub-block steps (32 keys each) ----
+    // MFMA A-operand fragments from LDS: K rows (32 keys x 16 dims per MFMA)
+    // and V^T rows (32 dims x 16 keys per MFMA).
+    // K: lane reads chunk (2*ks + hf) of key kb*32 + l32 (16 bytes). The
+    // swizzle depends on the key only modulo 32, so the per-lane byte offsets
+    // are fixed for the whole tile.
+    int koff[T::KS];
 #pragma unroll
-        for (int kb = 0; kb < T::KB; ++kb) {
-            if (kb * 32 >= nk) break;
-            // S^T for 32 keys x (QB*32) query rows
-            f32x16 s[QB];
+    for (int ks = 0; ks < T::KS; ++ks) koff[ks] = l32 * T::ROWB + (((2 * ks + hf) ^ k_swz<D>(l32)) << 4);
+    auto load_k = [&](const char* kl, int kb, bf16x8 (&ka)[T::KS]) {
+        const char* blk = kl + kb * 32 * T::ROWB;
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(blk + koff[ks]);
+    };
+    // V^T fragment for keys [kb*32 + 16*k2, +16) and dims [db*32, +32): two
+    // transposing 8-byte reads. In each 16-lane group, lane j receives element
+    // j%4 of the 8-byte rows read by lanes 4t + j/4 (t = 0..3); reading key
+    // kb*32 + 16*k2 + 8*r + 4*hf + (lane/4)%4 at dims db*32 + 16*((lane/16)%2)
+    // + 4*(lane%4) therefore hands lane l the dims l%32 of the keys that its
+    // P operand slots 4r..4r+3 hold.
+    const int vkey = 4 * hf + ((lane >> 2) & 3);        // key offset within 8 (per lane)
+    const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // the V swizzle depends on the key only modulo 8: fixed per-lane offsets
+    int voff[T::DB];
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+        const int d = db * 32 + vdim;
+        voff[db] = vkey * T::ROWB + (((d >> 3) ^ v_swz<D>(vkey)) << 4) + (d & 4) * 2;
+    }
+    auto load_v = [&](const char* vl, int kb, bf16x8 (&va)[2][T::DB]) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db) {
+                i16x4 half[2];
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const char* p = vl + (kb * 32 + k2 * 16 + r * 8) * T::ROWB + voff[db];
+                    half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4*)p);
+                }
+                const i16x8 both = {half[0][0], half[0][1], half[0][2], half[0][3],
+                                    half[1][0], half[1][1], half[1][2], half[1][3]};
+                va[k2][db] = __builtin_bit_cast(bf16x8, both);
+            }
+    };
+    // S^T for 32 keys x (QB*32) query rows
+    auto qk = [&](const bf16x8 (&ka)[T::KS], f32x16 (&sc)[QB]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sc[qb][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
+                sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[qb][ks], sc[qb], 0, 0, 0);
+    };
+    // keys at or past nk (segment end) get -inf; element e of a lane holds key
+    // kb*32 + 8*(e/4) + 4*hf + e%4
+    auto mask = [&](int kb, int32_t nk, f32x16 (&sc)[QB]) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) s[qb][e] = 0.f;
-            bf16x8 ka[T::KS];
+        for (int e = 0; e < 16; ++e) {
+            const bool dead = kb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3) >= nk;
 #pragma unroll
-            for (int ks = 0; ks < T::KS; ++ks)
-                ka[ks] = *reinterpret_cast<const bf16x8*>(kl + (kb * 32 + l32) * T::KP + (ks * 16 + hf * 8) * 2);
+            for (int qb = 0; qb < QB; ++qb) sc[qb][e] = dead ? -INFINITY : sc[qb][e];
+        }
+    };
+    // Online softmax against a lazily moved reference m_i: the weights are
+    // p = exp2(c*s - c*m_i). Every p is bounded by its lane's partial row sum,
+    // so while each lane's sum stays <= kPsumMax nothing can overflow and the
+    // reference may stay where it is. Otherwise (the first block, m_i = -inf;
+    // or a row max that grew by more than log2(kPsumMax) base-2 units) the wave
+    // takes this block's row maximum, moves m_i up to it, rescales O and l by
+    // exp2(c*(m_old - m_new)) and recomputes p (fix_reference). Same softmax;
+    // the common path has neither a max reduction nor an accumulator rescale.
+    auto weights = [&](const f32x16 (&sc)[QB], bf16x8 (&pk)[QB][2], float (&psum)[QB]) {
 #pragma unroll
-            for (int ks = 0; ks < T::KS; ++ks)
+        for (int qb = 0; qb < QB; ++qb) {
+            float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][e], c, -mc_i[qb]));
+                if (e & 1)
+                    acc1 += p;
+                else
+                    acc0 += p;
+                pk[qb][e >> 3][e & 7] = (__bf16)p;
+            }
+            psum[qb] = acc0 + acc1;
+        }
+    };
+    auto over_limit = [&](const float (&psum)[QB]) {
+        bool over = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) over |= !(psum[qb] <= kPsumMax);  // NaN counts as over
+        return __builtin_amdgcn_ballot_w64(over) != 0;
+    };
+    auto fix_reference = [&](const f32x16 (&sc)[QB], bf16x8 (&pk)[QB][2], float (&psum)[QB]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float v = sc[qb][0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) v = fmaxf(v, sc[qb][e]);
+            const float mnew = fmaxf(m_i[qb], fmaxf(v, __shfl_xor(v, 32)));
+            const float alpha = __builtin_amdgcn_exp2f((m_i[qb] - mnew) * c);
+            l_i[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
+            m_i[qb] = mnew;
+            mc_i[qb] = mnew * c;
+        }
+        weights(sc, pk, psum);
+    };
+    // O^T += V^T P^T over 32 keys: two 16-key MFMA steps per column block
+    auto pv = [&](const bf16x8 (&va)[2][T::DB], const bf16x8 (&pk)[QB][2]) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[qb][ks], s[qb], 0, 0, 0);
-            if (nk < (kb + 1) * 32) {
-                // keys past the segment end: element e holds key kb*32 + 8*(e/4) + 4*hf + e%4
+                    o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k2][db], pk[qb][k2], o[qb][db], 0, 0, 0);
+    };
+
+    // One K/V stage, software-pipelined inside the wave. The LDS fragments a
+    // step needs are read one scheduling region ahead of it (the rare
+    // reference branch fences regions, so the reads cannot sink back to their
+    // uses): region kb holds the V reads for PV(kb), the K reads and MFMAs of
+    // QK(kb+1) and the softmax VALU work of sub-block kb; PV(kb) opens the next
+    // region. `last` (compile-time) masks keys past the segment end; only the
+    // final stage of a segment needs it.
+    auto stage = [&](int buf, auto last, int32_t nk) {
+        constexpr bool LAST = decltype(last)::value;
+        const char* kl = lds + buf * T::STAGE;
+        const char* vl = kl + T::KBYTES;
+        f32x16 sc[2][QB];
+        bf16x8 ka[T::KS];
+        load_k(kl, 0, ka);
+        qk(ka, sc[0]);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = kb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-                    if (key >= nk)
-#pragma unroll
-                        for (int qb = 0; qb < QB; ++qb) s[qb][e] = -INFINITY;
-                }
+        for (int kb = 0; kb < T::KB; ++kb) {
+            if (LAST) mask(kb, nk, sc[kb & 1]);
+            bf16x8 va[2][T::DB];
+            load_v(vl, kb, va);
+            if (kb + 1 < T::KB) {
+                load_k(kl, kb + 1, ka);
+                qk(ka, sc[(kb + 1) & 1]);
             }
-            // Online softmax against a lazily moved reference max m_i: the
-            // weights are p = exp2(c*s - c*m_i). Every p is bounded by its row's
-            // partial sum, so while each lane's sum stays <= kPsumMax nothing
-            // can overflow and the reference may stay where it is. Otherwise
-            // (first block, m_i = -inf; or a row max that grew by more than
-            // log2(kPsumMax)) the wave takes this block's row max, rescales O and
-            // l by exp2(c*(m_old - m_new)) and recomputes p. Same softmax; the
-            // common path has neither a max reduction nor an accumulator rescale.
             bf16x8 pk[QB][2];
             float psum[QB];
-            auto weights = [&]() {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    float acc = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][e], c, -mc_i[qb]));
-                        acc += p;
-                        pk[qb][e >> 3][e & 7] = (__bf16)p;
-                    }
-                    psum[qb] = acc;
-                }
-            };
-            weights();
-            bool over = false;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) over |= !(psum[qb] <= kPsumMax);  // NaN counts as over
-            if (__builtin_amdgcn_ballot_w64(over) != 0) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    float v = s[qb][0];
-#pragma unroll
-                    for (int e = 1; e < 16; ++e) v = fmaxf(v, s[qb][e]);
-                    const float mnew = fmaxf(m_i[qb], fmaxf(v, __shfl_xor(v, 32)));
-                    const float alpha = __builtin_amdgcn_exp2f((m_i[qb] - mnew) * c);
-                    l_i[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
-                    m_i[qb] = mnew;
-                    mc_i[qb] = mnew * c;
-                }
-                weights();
-            }
+            weights(sc[kb & 1], pk, psum);
+            if (over_limit(psum)) fix_reference(sc[kb & 1], pk, psum);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) l_i[qb] += psum[qb];
-            // O^T += V^T P^T over the 32 keys, two 16-key MFMA steps
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-                for (int db = 0; db < T::DB; ++db) {
-                    const bf16x8 va = *reinterpret_cast<const bf16x8*>(vl + (db * 32 + l32) * T::VP + (kb * 32 + k2 * 16 + hf * 8) * 2);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[qb][k2], o[qb][db], 0, 0, 0);
-                }
+            pv(va, pk);
         }
-        if (more) store_tile(buf ^ 1);
-        __syncthreads();
-    }
+    };
 
-    // ---- epilogue: O = O_acc / l (bf16), LSE = m*scale + ln l ----
+    // ---- K/V loop: stage j computes while stage j+1 is fetched ----
+    if (nkt > 0) load_stage(0, 0);
+    // Every global load issued so far (Q fragments, first stage) is complete
+    // here; saying so also keeps the compiler's wait counters inside the loop
+    // from holding the MFMAs until the next stage's loads have landed.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
+    __syncthreads();
+    for (int32_t j = 0; j + 1 < nkt; ++j) {
+        load_stage(j + 1, (j + 1) & 1);
+        stage(j & 1, std::false_type{}, BN);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's share of stage j+1 is in LDS
+        __syncthreads();                     // ... and everyone's; stage j is no longer read
+    }
+    if (nkt > 0) stage((nkt - 1) & 1, std::true_type{}, lk - (nkt - 1) * BN);
+
+    // ---- epilogue: O = O_acc / l (bf16), LSE = ln sum exp(scale * s) ----
     const uint32_t o_rs = (uint32_t)(a.o_row * 2);
     char* optr = (char*)a.o + 2 * avf_elem_offset(q_tok0, a.o_row, h, a.o_head);
     const auto ors = make_rsrc(optr, (uint32_t)(rows_here - 1) * o_rs + 2 * D);
@@ -327,6 +395,7 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, ov), ors, off, 0, 0);
                 }
             if (hf == 0 && a.lse != nullptr) {
+                // natural-log LSE: m*scale + ln l (any reference m gives the same value)
                 const float lse = l_tot > 0.f ? m_i[qb] * a.scale + __logf(l_tot) : -INFINITY;
                 a.lse[(int64_t)h * a.lse_head + q_tok0 + row] = lse;
             }
@@ -345,13 +414,13 @@ hipError_t launch_cfg(const AvfLaunchArgs& a, hipStream_t stream) {
 // NW waves, BN keys per K/V stage). BM = QB * 32 * NW. Overridable at build
 // time (-DAVF_CFG_D128=QB,NW,BN) for tuning sweeps.
 #ifndef AVF_CFG_D64
-#define AVF_CFG_D64 1, 8, 64
+#define AVF_CFG_D64 1, 8, 128
 #endif
 #ifndef AVF_CFG_D96
-#define AVF_CFG_D96 1, 8, 64
+#define AVF_CFG_D96 1, 8, 128
 #endif
 #ifndef AVF_CFG_D128
-#define AVF_CFG_D128 1, 8, 64
+#define AVF_CFG_D128 1, 8, 128
 #endif
 template <int QB_, int NW_, int BN_>
 struct CfgOf { static constexpr int QB = QB_, NW = NW_, BN = BN_; };
