@@ -58,6 +58,12 @@ constexpr float kPsumMax = 65536.0f;
 // index stride; records are bytes and out-of-range loads return 0.
 constexpr int kBufWord3 = 0x00020000;
 
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n and leaves the
+// export and LGKM counters untouched.
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+    return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00;
+}
+
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                              kBufWord3);
@@ -65,13 +71,32 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 
 // 16-byte buffer load written straight to LDS: lane l of the wave fills
 // lds[16*l, 16*l + 16) (LDS base in M0, wave-uniform) with the record at
-// `voffset`. The builtin exists only for the device pass; the host pass must
-// not see it or it silently drops the kernel's launch stub.
-__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voffset) {
+// `voffset` of the buffer resource `rsrc`. It is issued as inline assembly on
+// purpose: the compiler then does not track it, so it adds no vector-memory
+// waits of its own before later LDS reads (it would otherwise make every
+// transposing read wait for the loads of later stages, which write other
+// buffers of the ring). Completion is awaited explicitly with s_waitcnt vmcnt
+// and a barrier before the stage is read. Vector-memory loads complete in
+// order, so the compiler's own waits on older loads stay correct.
+__device__ inline void load_lds16(i32x4 rsrc, const char* lds, uint32_t voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16,
-                                             voffset, 0, 0, 0);
+    const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voffset), "s"(rsrc)
+                 : "memory", "m0");
 #endif
+}
+
+// Buffer resource words (gfx9 layout) for the inline-assembly loads.
+__device__ inline i32x4 rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32) & 0xffff);  // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = kBufWord3;
+    return r;
 }
 
 // LDS rows of K and V are unpadded (2*D bytes); the 16-byte chunks of a row are
@@ -94,7 +119,7 @@ __device__ constexpr int v_swz(int key) {
     return D == 128 ? (key & 3) << 2 : D == 64 ? ((key >> 1) & 1) << 2 : 0;
 }
 
-template <int D, int QB, int NW, int BN>
+template <int D, int QB, int NW, int BN, int NBUF>
 struct Tile {
     static constexpr int NT = NW * 64;          // threads per workgroup
     static constexpr int BM = QB * 32 * NW;     // query rows per tile
@@ -106,14 +131,17 @@ struct Tile {
     static constexpr int STAGE = 2 * BN * ROWB; // K then V
     static constexpr int NI = BN * ROWB / 1024; // 1 KiB direct loads per array and stage
     static constexpr int NIW = (NI + NW - 1) / NW;
+    static constexpr int LPS = 2 * (NI / NW);   // direct loads per wave and stage (K and V)
     static_assert(D % 32 == 0 && BN % 32 == 0 && (BN * ROWB) % 1024 == 0, "tile shape");
+    static_assert(NI % NW == 0, "every wave issues the same number of loads per stage");
+    static_assert(NBUF >= 2 && NBUF * STAGE <= 160 * 1024, "LDS ring");
 };
 
-template <int D, int QB, int NW, int BN>
+template <int D, int QB, int NW, int BN, int NBUF>
 __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs a) {
-    using T = Tile<D, QB, NW, BN>;
+    using T = Tile<D, QB, NW, BN, NBUF>;
     constexpr int BM = T::BM;
-    __shared__ __attribute__((aligned(16))) char lds[2 * T::STAGE];
+    __shared__ __attribute__((aligned(16))) char lds[NBUF * T::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -180,14 +208,14 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
         const int32_t nk = min(BN, lk - key0);
         const char* kp = (const char*)a.k + 2 * avf_elem_offset(k_tok0 + key0, a.k_row, h, a.k_head);
         const char* vp = (const char*)a.v + 2 * avf_elem_offset(k_tok0 + key0, a.v_row, h, a.v_head);
-        const auto krs = make_rsrc(kp, (uint32_t)(nk - 1) * k_rs + 2 * D);
-        const auto vrs = make_rsrc(vp, (uint32_t)(nk - 1) * v_rs + 2 * D);
+        const i32x4 krs = rsrc_words(kp, (uint32_t)(nk - 1) * k_rs + 2 * D);
+        const i32x4 vrs = rsrc_words(vp, (uint32_t)(nk - 1) * v_rs + 2 * D);
         char* kl = lds + buf * T::STAGE;
         char* vl = kl + T::KBYTES;
 #pragma unroll
         for (int m = 0; m < T::NIW; ++m) {
             const int i = wave + NW * m;
-            if (T::NI % NW == 0 || i < T::NI) {
+            {
                 const int pos = i * 1024 + 16 * lane;
                 const int key = pos / T::ROWB;
                 const int slot = (pos % T::ROWB) >> 4;
@@ -359,20 +387,43 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
         }
     };
 
-    // ---- K/V loop: stage j computes while stage j+1 is fetched ----
-    if (nkt > 0) load_stage(0, 0);
-    // Every global load issued so far (Q fragments, first stage) is complete
-    // here; saying so also keeps the compiler's wait counters inside the loop
-    // from holding the MFMAs until the next stage's loads have landed.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
+    // ---- K/V loop: a ring of NBUF stage buffers; stage j lives in buffer
+    // j % NBUF and its loads are issued NBUF-1 stages before it is computed.
+    // Before stage j+1 is read, a wave waits until at most the loads of the
+    // stages after j+1 are outstanding (vector-memory loads complete in
+    // order), then the barrier makes every wave's share visible and retires
+    // the buffer of stage j for reuse.
+    constexpr int AHEAD = NBUF - 1;
+    auto wait_loads = [&](int later_stages) {  // later_stages in [0, AHEAD-1], wave-uniform
+        if (later_stages <= 0)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        else if (AHEAD - 1 >= 1 && later_stages == 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(1 * T::LPS));
+        else if (AHEAD - 1 >= 2 && later_stages == 2)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * T::LPS));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * T::LPS));
+    };
+    static_assert(AHEAD - 1 <= 3 && 3 * T::LPS <= 63, "vmcnt range");
+    const int32_t pre = min(AHEAD, nkt);
+    for (int32_t s0 = 0; s0 < pre; ++s0) load_stage(s0, s0);
+    // Wait for everything issued so far (Q fragments and the first stages),
+    // once per tile: the compiler does not see the stage loads, so only a full
+    // vmcnt(0) tells it that the Q fragments have landed; otherwise it would
+    // hold the loop's MFMAs on the in-flight loads of later stages.
+    wait_loads(0);
     __syncthreads();
+    int buf = 0;                  // j % NBUF
+    int ahead_buf = AHEAD % NBUF; // (j + AHEAD) % NBUF
     for (int32_t j = 0; j + 1 < nkt; ++j) {
-        load_stage(j + 1, (j + 1) & 1);
-        stage(j & 1, std::false_type{}, BN);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's share of stage j+1 is in LDS
-        __syncthreads();                     // ... and everyone's; stage j is no longer read
+        if (j + AHEAD < nkt) load_stage(j + AHEAD, ahead_buf);
+        stage(buf, std::false_type{}, BN);
+        wait_loads(min(AHEAD - 1, nkt - 2 - j));
+        __syncthreads();
+        buf = buf + 1 == NBUF ? 0 : buf + 1;
+        ahead_buf = ahead_buf + 1 == NBUF ? 0 : ahead_buf + 1;
     }
-    if (nkt > 0) stage((nkt - 1) & 1, std::true_type{}, lk - (nkt - 1) * BN);
+    if (nkt > 0) stage(buf, std::true_type{}, lk - (nkt - 1) * BN);
 
     // ---- epilogue: O = O_acc / l (bf16), LSE = ln sum exp(scale * s) ----
     const uint32_t o_rs = (uint32_t)(a.o_row * 2);
@@ -403,27 +454,28 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     }
 }
 
-template <int D, int QB, int NW, int BN>
+template <int D, int QB, int NW, int BN, int NBUF>
 hipError_t launch_cfg(const AvfLaunchArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN>), dim3((uint32_t)a.num_tiles), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, NBUF>), dim3((uint32_t)a.num_tiles), dim3(NW * 64), 0,
                        stream, a);
     return hipGetLastError();
 }
 
 // Per head_dim tile configuration: (QB query blocks of 32 rows per wave,
-// NW waves, BN keys per K/V stage). BM = QB * 32 * NW. Overridable at build
-// time (-DAVF_CFG_D128=QB,NW,BN) for tuning sweeps.
+// NW waves, BN keys per K/V stage, NBUF stages in the LDS ring).
+// BM = QB * 32 * NW. Overridable at build time (-DAVF_CFG_D128=QB,NW,BN,NBUF)
+// for tuning sweeps.
 #ifndef AVF_CFG_D64
-#define AVF_CFG_D64 1, 8, 128
+#define AVF_CFG_D64 1, 8, 128, 2
 #endif
 #ifndef AVF_CFG_D96
-#define AVF_CFG_D96 1, 8, 128
+#define AVF_CFG_D96 1, 8, 128, 2
 #endif
 #ifndef AVF_CFG_D128
-#define AVF_CFG_D128 1, 8, 128
+#define AVF_CFG_D128 1, 8, 128, 2
 #endif
-template <int QB_, int NW_, int BN_>
-struct CfgOf { static constexpr int QB = QB_, NW = NW_, BN = BN_; };
+template <int QB_, int NW_, int BN_, int NBUF_>
+struct CfgOf { static constexpr int QB = QB_, NW = NW_, BN = BN_, NBUF = NBUF_; };
 template <int D> struct Cfg;
 template <> struct Cfg<64> : CfgOf<AVF_CFG_D64> {};
 template <> struct Cfg<96> : CfgOf<AVF_CFG_D96> {};
@@ -445,9 +497,9 @@ int32_t avf_block_m(int32_t head_dim) {
 
 hipError_t avf_launch(const AvfLaunchArgs& a, int32_t head_dim, hipStream_t stream) {
     switch (head_dim) {
-        case 64: return launch_cfg<64, Cfg<64>::QB, Cfg<64>::NW, Cfg<64>::BN>(a, stream);
-        case 96: return launch_cfg<96, Cfg<96>::QB, Cfg<96>::NW, Cfg<96>::BN>(a, stream);
-        case 128: return launch_cfg<128, Cfg<128>::QB, Cfg<128>::NW, Cfg<128>::BN>(a, stream);
+        case 64: return launch_cfg<64, Cfg<64>::QB, Cfg<64>::NW, Cfg<64>::BN, Cfg<64>::NBUF>(a, stream);
+        case 96: return launch_cfg<96, Cfg<96>::QB, Cfg<96>::NW, Cfg<96>::BN, Cfg<96>::NBUF>(a, stream);
+        case 128: return launch_cfg<128, Cfg<128>::QB, Cfg<128>::NW, Cfg<128>::BN, Cfg<128>::NBUF>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
