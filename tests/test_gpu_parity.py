@@ -76,6 +76,14 @@ SMALL = {
     "cross_long_k": custom("cross_long_k", 2, 128, [0, 5, 705], [0, 2000, 2130], std=0.5),
     "self_tiles_d96": custom("self_tiles_d96", 4, 96, [0, 256, 257, 769], std=0.1),
 }
+# Key lengths from one stage of 128 keys to nine, each stage count with and
+# without a ragged tail: every position of the K (2) and V (3) buffer rings,
+# and the first and last stages, meet in some segment.
+_RING_LK = [1, 31, 128, 129, 255, 256, 300, 384, 400, 512, 513, 640, 700, 768, 896, 1000, 1024, 1152]
+for _d in (64, 96, 128):
+    _ck = np.concatenate([[0], np.cumsum(_RING_LK)]).tolist()
+    _cq = [37 * i for i in range(len(_RING_LK) + 1)]
+    SMALL[f"ring_stages_d{_d}"] = custom(f"ring_stages_d{_d}", 2, _d, _cq, _ck, std=1.0)
 
 
 @pytest.mark.parametrize("name", sorted(SMALL))

@@ -1,9 +1,10 @@
 // Packed variable-length attention forward for gfx950 (MI355X, CDNA4).
 //
 // One workgroup computes one tile: BM query rows of one head of one segment,
-// streaming that segment's K/V in stages of BN keys through double-buffered
-// LDS. K and V reach LDS by buffer loads that write LDS directly (no
-// registers, no LDS store instructions), one stage ahead of the compute. The operation is the flash-attention varlen forward with its LSE
+// streaming that segment's K/V in stages of BN keys through rings of LDS
+// buffers. K and V reach LDS by buffer loads that write LDS directly (no
+// registers, no LDS store instructions), one stage ahead of the compute.
+// The operation is the flash-attention varlen forward with its LSE
 // (the (out, lse) return of flash_attn_varlen_func on the "[FA4] cute varlen
 // backward: int32 overflow in _bwd_preprocess ..." page); the online softmax
 // keeps a running row maximum m and sum l and rescales the accumulator when m
@@ -43,6 +44,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -69,8 +71,8 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
                                              kBufWord3);
 }
 
-// 16-byte buffer load written straight to LDS: lane l of the wave fills
-// lds[16*l, 16*l + 16) (LDS base in M0, wave-uniform) with the record at
+// 16-byte buffer load written straight to LDS: lane l of the wave fills LDS
+// bytes [lds_addr + 16*l, +16) (lds_addr in M0, wave-uniform) with the record at
 // `voffset` of the buffer resource `rsrc`. It is issued as inline assembly on
 // purpose: the compiler then does not track it, so it adds no vector-memory
 // waits of its own before later LDS reads (it would otherwise make every
@@ -78,14 +80,22 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 // buffers of the ring). Completion is awaited explicitly with s_waitcnt vmcnt
 // and a barrier before the stage is read. Vector-memory loads complete in
 // order, so the compiler's own waits on older loads stay correct.
-__device__ inline void load_lds16(i32x4 rsrc, const char* lds, uint32_t voffset) {
+__device__ inline void load_lds16(i32x4 rsrc, uint32_t lds_addr, uint32_t voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds;
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
-                 : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voffset), "s"(rsrc)
-                 : "memory", "m0");
+                 : "v"(voffset), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "memory");
 #endif
+}
+
+// Marks `x` as read and rewritten at this point of the instruction stream
+// (emits nothing). Between scheduling fences this keeps a pure arithmetic
+// result where the source computes it instead of letting the optimizer sink
+// it to its first use.
+template <typename V>
+__device__ inline void pin(V& x) {
+    asm volatile("" : "+v"(x));
 }
 
 // Buffer resource words (gfx9 layout) for the inline-assembly loads.
@@ -119,29 +129,36 @@ __device__ constexpr int v_swz(int key) {
     return D == 128 ? (key & 3) << 2 : D == 64 ? ((key >> 1) & 1) << 2 : 0;
 }
 
-template <int D, int QB, int NW, int BN, int NBUF>
+// LDS holds a ring of KBUF K stages followed by a ring of VBUF V stages. V
+// lives one stage longer than K because each wave's P.V product trails its
+// Q.K^T product by one 32-key sub-block, across stage boundaries.
+template <int D, int QB, int NW, int BN>
 struct Tile {
     static constexpr int NT = NW * 64;          // threads per workgroup
     static constexpr int BM = QB * 32 * NW;     // query rows per tile
     static constexpr int KS = D / 16;           // MFMA k-steps over D
     static constexpr int DB = D / 32;           // 32-wide column blocks of O
-    static constexpr int KB = BN / 32;          // 32-key sub-blocks per K/V tile
+    static constexpr int KB = BN / 32;          // 32-key sub-blocks per K/V stage
     static constexpr int ROWB = D * 2;          // bytes per K/V row in LDS
-    static constexpr int KBYTES = BN * ROWB;    // K part of a stage
-    static constexpr int STAGE = 2 * BN * ROWB; // K then V
-    static constexpr int NI = BN * ROWB / 1024; // 1 KiB direct loads per array and stage
-    static constexpr int NIW = (NI + NW - 1) / NW;
-    static constexpr int LPS = 2 * (NI / NW);   // direct loads per wave and stage (K and V)
-    static_assert(D % 32 == 0 && BN % 32 == 0 && (BN * ROWB) % 1024 == 0, "tile shape");
+    static constexpr int SBYTES = BN * ROWB;    // one stage of K (or of V)
+    static constexpr int KBUF = 2, VBUF = 3;
+    static constexpr int LDS_BYTES = (KBUF + VBUF) * SBYTES;
+    static constexpr int NI = SBYTES / 1024;    // 1 KiB direct loads per array and stage
+    static constexpr int NIW = NI / NW;         // ... per wave
+    static constexpr int LPS = 2 * NIW;         // direct loads per wave and stage (K and V)
+    static_assert(D % 32 == 0 && BN % 32 == 0 && SBYTES % 1024 == 0, "tile shape");
+    static_assert(KB >= 4 && KB % 2 == 0, "four or more sub-blocks per stage, parity repeating every stage");
     static_assert(NI % NW == 0, "every wave issues the same number of loads per stage");
-    static_assert(NBUF >= 2 && NBUF * STAGE <= 160 * 1024, "LDS ring");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS rings");
 };
 
-template <int D, int QB, int NW, int BN, int NBUF>
+template <int D, int QB, int NW, int BN>
 __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs a) {
-    using T = Tile<D, QB, NW, BN, NBUF>;
+    using T = Tile<D, QB, NW, BN>;
     constexpr int BM = T::BM;
-    __shared__ __attribute__((aligned(16))) char lds[NBUF * T::STAGE];
+    __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+    // LDS byte address of the array (M0 operand of the direct loads)
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -203,26 +220,24 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     const int32_t nkt = (lk + BN - 1) / BN;
     const uint32_t k_rs = (uint32_t)(a.k_row * 2);
     const uint32_t v_rs = (uint32_t)(a.v_row * 2);
-    auto load_stage = [&](int32_t j, int buf) {
+    auto load_stage = [&](int32_t j, int kbuf, int vbuf) {
         const int32_t key0 = j * BN;
         const int32_t nk = min(BN, lk - key0);
         const char* kp = (const char*)a.k + 2 * avf_elem_offset(k_tok0 + key0, a.k_row, h, a.k_head);
         const char* vp = (const char*)a.v + 2 * avf_elem_offset(k_tok0 + key0, a.v_row, h, a.v_head);
         const i32x4 krs = rsrc_words(kp, (uint32_t)(nk - 1) * k_rs + 2 * D);
         const i32x4 vrs = rsrc_words(vp, (uint32_t)(nk - 1) * v_rs + 2 * D);
-        char* kl = lds + buf * T::STAGE;
-        char* vl = kl + T::KBYTES;
+        const uint32_t kl = lds_addr + kbuf * T::SBYTES;
+        const uint32_t vl = lds_addr + (T::KBUF + vbuf) * T::SBYTES;
 #pragma unroll
         for (int m = 0; m < T::NIW; ++m) {
             const int i = wave + NW * m;
-            {
-                const int pos = i * 1024 + 16 * lane;
-                const int key = pos / T::ROWB;
-                const int slot = (pos % T::ROWB) >> 4;
-                const uint32_t kc = (uint32_t)min(key, nk - 1);
-                load_lds16(krs, kl + i * 1024, kc * k_rs + ((slot ^ k_swz<D>(key)) << 4));
-                load_lds16(vrs, vl + i * 1024, kc * v_rs + ((slot ^ v_swz<D>(key)) << 4));
-            }
+            const int pos = i * 1024 + 16 * lane;
+            const int key = pos / T::ROWB;
+            const int slot = (pos % T::ROWB) >> 4;
+            const uint32_t kc = (uint32_t)min(key, nk - 1);
+            load_lds16(krs, kl + i * 1024, kc * k_rs + ((slot ^ k_swz<D>(key)) << 4));
+            load_lds16(vrs, vl + i * 1024, kc * v_rs + ((slot ^ v_swz<D>(key)) << 4));
         }
     };
 
@@ -353,77 +368,179 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
                     o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k2][db], pk[qb][k2], o[qb][db], 0, 0, 0);
     };
 
-    // One K/V stage, software-pipelined inside the wave. The LDS fragments a
-    // step needs are read one scheduling region ahead of it (the rare
-    // reference branch fences regions, so the reads cannot sink back to their
-    // uses): region kb holds the V reads for PV(kb), the K reads and MFMAs of
-    // QK(kb+1) and the softmax VALU work of sub-block kb; PV(kb) opens the next
-    // region. `last` (compile-time) masks keys past the segment end; only the
-    // final stage of a segment needs it.
-    auto stage = [&](int buf, auto last, int32_t nk) {
+    // Software pipeline inside the wave, continuous over the whole key
+    // sequence. Iteration g (32-key sub-block g) issues the MFMAs of Q.K^T for
+    // sub-block g+1 and of P.V for sub-block g-1 while its VALU work is the
+    // softmax of sub-block g, whose scores Q.K^T(g) finished during iteration
+    // g-1; so neither product waits for the softmax and the softmax never
+    // waits for a product. The iteration is written slot by slot with a
+    // scheduling fence between slots: slot t issues one MFMA and a share of
+    // the softmax, so every MFMA has independent VALU work behind it and the
+    // MFMA pipe, shared by the SIMD's waves, stays fed.
+    // Fragments rotate through one set of KS registers (Q.K^T and P.V both
+    // take KS = D/16 MFMAs per sub-block): slot t < KS consumes K fragment t
+    // and refills its register with the V^T fragment that slot t + KS
+    // consumes; slot KS + u consumes that V^T fragment and refills the
+    // register with K fragment u of the next iteration. Every LDS read thus
+    // has KS slots to land.
+    // The rare reference move (fix_reference) rescales O after the P.V(g-1)
+    // MFMAs, so O then holds all earlier sub-blocks against the old reference.
+    //
+    // Staging: stage j (BN keys) sits in K buffer j % 2 and V buffer j % 3.
+    // The one barrier per stage is at the top of its sub-block KB-2, the
+    // first iteration that reads K fragments of stage j+1: there each wave
+    // first waits for its share of stage j+1 (loaded one stage earlier), and
+    // after it every wave is past its last read of K stage j (during
+    // sub-block KB-3) and of V stage j-1 (during sub-block 0 of stage j), so
+    // stage j+2 is loaded into exactly those two buffers.
+    f32x16 sc[2][QB];      // scores of sub-blocks with even / odd index
+    bf16x8 pk[2][QB][2];   // their weights as bf16 P^T operands
+    bf16x8 fr[T::KS];      // rotating K / V^T fragment registers
+    const char* kring = lds;
+    const char* vring = lds + T::KBUF * T::SBYTES;
+    auto read_k = [&](const char* blk, int u) {
+        return *reinterpret_cast<const bf16x8*>(blk + koff[u]);
+    };
+    // V^T fragment u = k2 * DB + db of the sub-block at `blk`
+    auto read_v = [&](const char* blk, int u) {
+        const int k2 = u / T::DB, db = u % T::DB;
+        i16x4 half[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const char* p = blk + (k2 * 16 + r * 8) * T::ROWB + voff[db];
+            half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+        }
+        const i16x8 both = {half[0][0], half[0][1], half[0][2], half[0][3],
+                            half[1][0], half[1][1], half[1][2], half[1][3]};
+        return __builtin_bit_cast(bf16x8, both);
+    };
+    // vblk: V sub-block g-1; kblk: K sub-block g+2 (refill_k false when there
+    // is none)
+    auto iterate = [&](const f32x16 (&sv)[QB], f32x16 (&snext)[QB], bool do_qk, const bf16x8 (&pprev)[QB][2],
+                       bf16x8 (&pcur)[QB][2], float (&psum)[QB], const char* vblk, const char* kblk,
+                       bool refill_k) {
+        constexpr int NSLOT = 2 * T::KS;
+        float acc[QB][2], pe[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][0] = acc[qb][1] = 0.f;
+#pragma unroll
+        for (int t = 0; t < NSLOT; ++t) {
+            if (t < T::KS) {
+                if (do_qk) {
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        const f32x16 zero = {};
+                        snext[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[t], qf[qb][t], t == 0 ? zero : snext[qb],
+                                                                            0, 0, 0);
+                    }
+                }
+                fr[t] = read_v(vblk, t);
+            } else {
+                const int u = t - T::KS, k2 = u / T::DB, db = u % T::DB;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[u], pprev[qb][k2], o[qb][db], 0, 0, 0);
+                if (refill_k) fr[u] = read_k(kblk, u);
+            }
+#pragma unroll
+            for (int e = t * 16 / NSLOT; e < (t + 1) * 16 / NSLOT; ++e)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[qb][e], c, -mc_i[qb]));
+                    acc[qb][e & 1] += p;
+                    pin(acc[qb][e & 1]);
+                    if (e & 1) {
+                        bf16x2 w = {(__bf16)pe[qb], (__bf16)p};
+                        pin(w);
+                        pcur[qb][e >> 3][(e & 7) - 1] = w[0];
+                        pcur[qb][e >> 3][e & 7] = w[1];
+                    } else {
+                        pe[qb] = p;
+                    }
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) psum[qb] = acc[qb][0] + acc[qb][1];
+    };
+
+    // `last` (compile-time) marks the segment's final stage: keys past the
+    // segment end are masked and there is no next stage. vprev is the V
+    // buffer of stage j-1 (for j = 0 any loaded one: its P.V weights are
+    // zero), vnext the one stage j+2 is loaded into.
+    auto stage = [&](int32_t j, int kbuf, int vbuf, int vprev, int vnext, auto last, int32_t nk) {
         constexpr bool LAST = decltype(last)::value;
-        const char* kl = lds + buf * T::STAGE;
-        const char* vl = kl + T::KBYTES;
-        f32x16 sc[2][QB];
-        bf16x8 ka[T::KS];
-        load_k(kl, 0, ka);
-        qk(ka, sc[0]);
+        const char* kl = kring + kbuf * T::SBYTES;
+        const char* vl = vring + vbuf * T::SBYTES;
+        constexpr int SUB = 32 * T::ROWB;  // bytes per 32-key sub-block
 #pragma unroll
         for (int kb = 0; kb < T::KB; ++kb) {
-            if (LAST) mask(kb, nk, sc[kb & 1]);
-            bf16x8 va[2][T::DB];
-            load_v(vl, kb, va);
-            if (kb + 1 < T::KB) {
-                load_k(kl, kb + 1, ka);
-                qk(ka, sc[(kb + 1) & 1]);
+            if (kb == T::KB - 2 && !LAST) {
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                __syncthreads();
+                if (j + 2 < nkt) load_stage(j + 2, kbuf, vnext);
             }
-            bf16x8 pk[QB][2];
+            if (LAST) mask(kb, nk, sc[kb & 1]);
+            const char* vblk = kb > 0 ? vl + (kb - 1) * SUB : vring + vprev * T::SBYTES + (T::KB - 1) * SUB;
+            const bool next_here = kb + 2 < T::KB;
+            const char* kblk = next_here ? kl + (kb + 2) * SUB : kring + (kbuf ^ 1) * T::SBYTES + (kb + 2 - T::KB) * SUB;
             float psum[QB];
-            weights(sc[kb & 1], pk, psum);
-            if (over_limit(psum)) fix_reference(sc[kb & 1], pk, psum);
+            // sub-block g-1 has the other parity
+            iterate(sc[kb & 1], sc[(kb + 1) & 1], !(LAST && kb == T::KB - 1), pk[(kb + 1) & 1], pk[kb & 1], psum,
+                    vblk, kblk, next_here || !LAST);
+            if (over_limit(psum)) fix_reference(sc[kb & 1], pk[kb & 1], psum);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) l_i[qb] += psum[qb];
-            pv(va, pk);
+        }
+        if (LAST) {
+            // P.V of the segment's final sub-block
+#pragma unroll
+            for (int u = 0; u < T::KS; ++u) fr[u] = read_v(vl + (T::KB - 1) * SUB, u);
+#pragma unroll
+            for (int u = 0; u < T::KS; ++u)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    o[qb][u % T::DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[u], pk[(T::KB - 1) & 1][qb][u / T::DB],
+                                                                              o[qb][u % T::DB], 0, 0, 0);
         }
     };
 
-    // ---- K/V loop: a ring of NBUF stage buffers; stage j lives in buffer
-    // j % NBUF and its loads are issued NBUF-1 stages before it is computed.
-    // Before stage j+1 is read, a wave waits until at most the loads of the
-    // stages after j+1 are outstanding (vector-memory loads complete in
-    // order), then the barrier makes every wave's share visible and retires
-    // the buffer of stage j for reuse.
-    constexpr int AHEAD = NBUF - 1;
-    auto wait_loads = [&](int later_stages) {  // later_stages in [0, AHEAD-1], wave-uniform
-        if (later_stages <= 0)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        else if (AHEAD - 1 >= 1 && later_stages == 1)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(1 * T::LPS));
-        else if (AHEAD - 1 >= 2 && later_stages == 2)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * T::LPS));
-        else
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * T::LPS));
-    };
-    static_assert(AHEAD - 1 <= 3 && 3 * T::LPS <= 63, "vmcnt range");
-    const int32_t pre = min(AHEAD, nkt);
-    for (int32_t s0 = 0; s0 < pre; ++s0) load_stage(s0, s0);
-    // Wait for everything issued so far (Q fragments and the first stages),
-    // once per tile: the compiler does not see the stage loads, so only a full
-    // vmcnt(0) tells it that the Q fragments have landed; otherwise it would
-    // hold the loop's MFMAs on the in-flight loads of later stages.
-    wait_loads(0);
-    __syncthreads();
-    int buf = 0;                  // j % NBUF
-    int ahead_buf = AHEAD % NBUF; // (j + AHEAD) % NBUF
-    for (int32_t j = 0; j + 1 < nkt; ++j) {
-        if (j + AHEAD < nkt) load_stage(j + AHEAD, ahead_buf);
-        stage(buf, std::false_type{}, BN);
-        wait_loads(min(AHEAD - 1, nkt - 2 - j));
+    if (nkt > 0) {
+        load_stage(0, 0, 0);
+        if (nkt > 1) load_stage(1, 1, 1);
+        // Wait for everything issued so far (Q fragments and the first two
+        // stages), once per tile: the compiler does not see the stage loads,
+        // so only a full vmcnt(0) tells it that the Q fragments have landed;
+        // otherwise it would hold the loop's MFMAs on in-flight stage loads.
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
-        buf = buf + 1 == NBUF ? 0 : buf + 1;
-        ahead_buf = ahead_buf + 1 == NBUF ? 0 : ahead_buf + 1;
+        // S(0), then the K fragments of sub-block 1 for the first iteration
+        {
+            bf16x8 ka[T::KS];
+            load_k(kring, 0, ka);
+            qk(ka, sc[0]);
+        }
+#pragma unroll
+        for (int u = 0; u < T::KS; ++u) fr[u] = read_k(kring + 32 * T::ROWB, u);
+        // Sub-block 0 has no predecessor: its P.V slots multiply zero
+        // weights with loaded (finite) V rows instead, which keeps one
+        // branch-free body for every stage.
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pk[1][qb][0][e] = (__bf16)0.f;
+                pk[1][qb][1][e] = (__bf16)0.f;
+            }
+        int kbuf = 0, vbuf = 0, vprev = 0, vnext = 2;  // j % 2, j % 3, (j - 1) % 3, (j + 2) % 3
+        for (int32_t j = 0; j + 1 < nkt; ++j) {
+            stage(j, kbuf, vbuf, vprev, vnext, std::false_type{}, BN);
+            kbuf ^= 1;
+            vprev = vnext = vbuf;
+            vbuf = vbuf == 2 ? 0 : vbuf + 1;
+        }
+        stage(nkt - 1, kbuf, vbuf, vprev, vnext, std::true_type{}, lk - (nkt - 1) * BN);
     }
-    if (nkt > 0) stage(buf, std::true_type{}, lk - (nkt - 1) * BN);
 
     // ---- epilogue: O = O_acc / l (bf16), LSE = ln sum exp(scale * s) ----
     const uint32_t o_rs = (uint32_t)(a.o_row * 2);
@@ -454,28 +571,26 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     }
 }
 
-template <int D, int QB, int NW, int BN, int NBUF>
+template <int D, int QB, int NW, int BN>
 hipError_t launch_cfg(const AvfLaunchArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, NBUF>), dim3((uint32_t)a.num_tiles), dim3(NW * 64), 0,
-                       stream, a);
+    hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN>), dim3((uint32_t)a.num_tiles), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 // Per head_dim tile configuration: (QB query blocks of 32 rows per wave,
-// NW waves, BN keys per K/V stage, NBUF stages in the LDS ring).
-// BM = QB * 32 * NW. Overridable at build time (-DAVF_CFG_D128=QB,NW,BN,NBUF)
-// for tuning sweeps.
+// NW waves, BN keys per K/V stage). BM = QB * 32 * NW. Overridable at build
+// time (-DAVF_CFG_D128=QB,NW,BN) for tuning sweeps.
 #ifndef AVF_CFG_D64
-#define AVF_CFG_D64 1, 8, 128, 2
+#define AVF_CFG_D64 1, 8, 128
 #endif
 #ifndef AVF_CFG_D96
-#define AVF_CFG_D96 1, 8, 128, 2
+#define AVF_CFG_D96 1, 8, 128
 #endif
 #ifndef AVF_CFG_D128
-#define AVF_CFG_D128 1, 8, 128, 2
+#define AVF_CFG_D128 1, 8, 128
 #endif
-template <int QB_, int NW_, int BN_, int NBUF_>
-struct CfgOf { static constexpr int QB = QB_, NW = NW_, BN = BN_, NBUF = NBUF_; };
+template <int QB_, int NW_, int BN_>
+struct CfgOf { static constexpr int QB = QB_, NW = NW_, BN = BN_; };
 template <int D> struct Cfg;
 template <> struct Cfg<64> : CfgOf<AVF_CFG_D64> {};
 template <> struct Cfg<96> : CfgOf<AVF_CFG_D96> {};
@@ -497,9 +612,9 @@ int32_t avf_block_m(int32_t head_dim) {
 
 hipError_t avf_launch(const AvfLaunchArgs& a, int32_t head_dim, hipStream_t stream) {
     switch (head_dim) {
-        case 64: return launch_cfg<64, Cfg<64>::QB, Cfg<64>::NW, Cfg<64>::BN, Cfg<64>::NBUF>(a, stream);
-        case 96: return launch_cfg<96, Cfg<96>::QB, Cfg<96>::NW, Cfg<96>::BN, Cfg<96>::NBUF>(a, stream);
-        case 128: return launch_cfg<128, Cfg<128>::QB, Cfg<128>::NW, Cfg<128>::BN, Cfg<128>::NBUF>(a, stream);
+        case 64: return launch_cfg<64, Cfg<64>::QB, Cfg<64>::NW, Cfg<64>::BN>(a, stream);
+        case 96: return launch_cfg<96, Cfg<96>::QB, Cfg<96>::NW, Cfg<96>::BN>(a, stream);
+        case 128: return launch_cfg<128, Cfg<128>::QB, Cfg<128>::NW, Cfg<128>::BN>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
