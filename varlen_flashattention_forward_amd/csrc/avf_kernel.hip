@@ -244,17 +244,15 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     // ---- per-sub-block steps (32 keys each) ----
     // MFMA A-operand fragments from LDS: K rows (32 keys x 16 dims per MFMA)
     // and V^T rows (32 dims x 16 keys per MFMA).
-    // K: lane reads chunk (2*ks + hf) of key kb*32 + l32 (16 bytes). The
-    // swizzle depends on the key only modulo 32, so the per-lane byte offsets
-    // are fixed for the whole tile.
-    int koff[T::KS];
+    // K: lane reads chunk (2*ks + hf) of key sub*32 + l32 (16 bytes). The
+    // swizzle depends on the key only modulo 32, so within a buffer the
+    // per-lane byte offsets are fixed; kcur holds them for the K buffer being
+    // read now and moves to the other buffer once per stage, so every
+    // fragment read is one LDS instruction with an immediate sub-block offset.
+    constexpr int SUB = 32 * T::ROWB;  // bytes per 32-key sub-block
+    int kcur[T::KS];
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) koff[ks] = l32 * T::ROWB + (((2 * ks + hf) ^ k_swz<D>(l32)) << 4);
-    auto load_k = [&](const char* kl, int kb, bf16x8 (&ka)[T::KS]) {
-        const char* blk = kl + kb * 32 * T::ROWB;
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(blk + koff[ks]);
-    };
+    for (int ks = 0; ks < T::KS; ++ks) kcur[ks] = l32 * T::ROWB + (((2 * ks + hf) ^ k_swz<D>(l32)) << 4);
     // V^T fragment for keys [kb*32 + 16*k2, +16) and dims [db*32, +32): two
     // transposing 8-byte reads. In each 16-lane group, lane j receives element
     // j%4 of the 8-byte rows read by lanes 4t + j/4 (t = 0..3); reading key
@@ -263,30 +261,15 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     // P operand slots 4r..4r+3 hold.
     const int vkey = 4 * hf + ((lane >> 2) & 3);        // key offset within 8 (per lane)
     const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    // the V swizzle depends on the key only modulo 8: fixed per-lane offsets
-    int voff[T::DB];
+    // The V swizzle depends on the key only modulo 8: fixed per-lane offsets
+    // within a buffer; vcur holds them for the V buffer being read now (the
+    // V ring starts after the K ring) and moves once per stage.
+    int vcur[T::DB];
 #pragma unroll
     for (int db = 0; db < T::DB; ++db) {
         const int d = db * 32 + vdim;
-        voff[db] = vkey * T::ROWB + (((d >> 3) ^ v_swz<D>(vkey)) << 4) + (d & 4) * 2;
+        vcur[db] = T::KBUF * T::SBYTES + vkey * T::ROWB + (((d >> 3) ^ v_swz<D>(vkey)) << 4) + (d & 4) * 2;
     }
-    auto load_v = [&](const char* vl, int kb, bf16x8 (&va)[2][T::DB]) {
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-            for (int db = 0; db < T::DB; ++db) {
-                i16x4 half[2];
-#pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const char* p = vl + (kb * 32 + k2 * 16 + r * 8) * T::ROWB + voff[db];
-                    half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4*)p);
-                }
-                const i16x8 both = {half[0][0], half[0][1], half[0][2], half[0][3],
-                                    half[1][0], half[1][1], half[1][2], half[1][3]};
-                va[k2][db] = __builtin_bit_cast(bf16x8, both);
-            }
-    };
     // S^T for 32 keys x (QB*32) query rows
     auto qk = [&](const bf16x8 (&ka)[T::KS], f32x16 (&sc)[QB]) {
 #pragma unroll
@@ -396,35 +379,37 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     f32x16 sc[2][QB];      // scores of sub-blocks with even / odd index
     bf16x8 pk[2][QB][2];   // their weights as bf16 P^T operands
     bf16x8 fr[T::KS];      // rotating K / V^T fragment registers
-    const char* kring = lds;
-    const char* vring = lds + T::KBUF * T::SBYTES;
-    auto read_k = [&](const char* blk, int u) {
-        return *reinterpret_cast<const bf16x8*>(blk + koff[u]);
+    // K fragment u of sub-block `sub` of the K buffer being read
+    auto read_k = [&](int sub, int u) {
+        return *reinterpret_cast<const bf16x8*>(lds + kcur[u] + sub * SUB);
     };
-    // V^T fragment u = k2 * DB + db of the sub-block at `blk`
-    auto read_v = [&](const char* blk, int u) {
+    // V^T fragment u = k2 * DB + db of sub-block `sub` of the V buffer being read
+    auto read_v = [&](int sub, int u) {
         const int k2 = u / T::DB, db = u % T::DB;
         i16x4 half[2];
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-            const char* p = blk + (k2 * 16 + r * 8) * T::ROWB + voff[db];
+            const char* p = lds + vcur[db] + sub * SUB + (k2 * 16 + r * 8) * T::ROWB;
             half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
         }
         const i16x8 both = {half[0][0], half[0][1], half[0][2], half[0][3],
                             half[1][0], half[1][1], half[1][2], half[1][3]};
         return __builtin_bit_cast(bf16x8, both);
     };
-    // vblk: V sub-block g-1; kblk: K sub-block g+2 (refill_k false when there
-    // is none)
+    // vsub: V sub-block g-1; ksub: K sub-block g+2 (refill_k false when there
+    // is none), each in the buffer its address set points at
     auto iterate = [&](const f32x16 (&sv)[QB], f32x16 (&snext)[QB], bool do_qk, const bf16x8 (&pprev)[QB][2],
-                       bf16x8 (&pcur)[QB][2], float (&psum)[QB], const char* vblk, const char* kblk,
-                       bool refill_k) {
+                       bf16x8 (&pcur)[QB][2], float (&psum)[QB], int vsub, int ksub, bool refill_k) {
         constexpr int NSLOT = 2 * T::KS;
-        float acc[QB][2], pe[QB];
+        // Softmax element e (of the lane's 16 scores) belongs to slot
+        // e * NSLOT / 16; its three dependent steps run one slot apart: the
+        // scaled exponent in its slot, exp2 in the next, the row-sum add (and
+        // the bf16 packing of an element pair) in the one after. No VALU
+        // instruction then waits on a result of its own slot, and two extra
+        // VALU-only slots finish the tail.
+        float x[QB][16], pw[QB][16], acc[QB][2];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[qb][0] = acc[qb][1] = 0.f;
-#pragma unroll
-        for (int t = 0; t < NSLOT; ++t) {
+        for (int t = 0; t < NSLOT + 2; ++t) {
             if (t < T::KS) {
                 if (do_qk) {
 #pragma unroll
@@ -434,30 +419,37 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
                                                                             0, 0, 0);
                     }
                 }
-                fr[t] = read_v(vblk, t);
-            } else {
+                fr[t] = read_v(vsub, t);
+            } else if (t < NSLOT) {
                 const int u = t - T::KS, k2 = u / T::DB, db = u % T::DB;
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[u], pprev[qb][k2], o[qb][db], 0, 0, 0);
-                if (refill_k) fr[u] = read_k(kblk, u);
+                if (refill_k) fr[u] = read_k(ksub, u);
             }
 #pragma unroll
-            for (int e = t * 16 / NSLOT; e < (t + 1) * 16 / NSLOT; ++e)
+            for (int e = 0; e < 16; ++e) {
+                const int te = e * NSLOT / 16;
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[qb][e], c, -mc_i[qb]));
-                    acc[qb][e & 1] += p;
-                    pin(acc[qb][e & 1]);
-                    if (e & 1) {
-                        bf16x2 w = {(__bf16)pe[qb], (__bf16)p};
-                        pin(w);
-                        pcur[qb][e >> 3][(e & 7) - 1] = w[0];
-                        pcur[qb][e >> 3][e & 7] = w[1];
-                    } else {
-                        pe[qb] = p;
+                    if (t == te) {
+                        x[qb][e] = __builtin_fmaf(sv[qb][e], c, -mc_i[qb]);
+                        pin(x[qb][e]);
+                    } else if (t == te + 1) {
+                        pw[qb][e] = __builtin_amdgcn_exp2f(x[qb][e]);
+                        pin(pw[qb][e]);
+                    } else if (t == te + 2) {
+                        acc[qb][e & 1] = e < 2 ? pw[qb][e] : acc[qb][e & 1] + pw[qb][e];
+                        pin(acc[qb][e & 1]);
+                        if (e & 1) {
+                            bf16x2 w = {(__bf16)pw[qb][e - 1], (__bf16)pw[qb][e]};
+                            pin(w);
+                            pcur[qb][e >> 3][(e & 7) - 1] = w[0];
+                            pcur[qb][e >> 3][e & 7] = w[1];
+                        }
                     }
                 }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -465,29 +457,30 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     };
 
     // `last` (compile-time) marks the segment's final stage: keys past the
-    // segment end are masked and there is no next stage. vprev is the V
-    // buffer of stage j-1 (for j = 0 any loaded one: its P.V weights are
-    // zero), vnext the one stage j+2 is loaded into.
-    auto stage = [&](int32_t j, int kbuf, int vbuf, int vprev, int vnext, auto last, int32_t nk) {
+    // segment end are masked and there is no next stage. vnext is the V
+    // buffer stage j+2 is loaded into. At the barrier the K reads move on to
+    // stage j+1's buffer (kcur += kdelta); at sub-block 1 the V reads move
+    // from stage j-1's buffer to stage j's (vcur += vdelta).
+    auto stage = [&](int32_t j, int kbuf, int vnext, int kdelta, int vdelta, auto last, int32_t nk) {
         constexpr bool LAST = decltype(last)::value;
-        const char* kl = kring + kbuf * T::SBYTES;
-        const char* vl = vring + vbuf * T::SBYTES;
-        constexpr int SUB = 32 * T::ROWB;  // bytes per 32-key sub-block
 #pragma unroll
         for (int kb = 0; kb < T::KB; ++kb) {
             if (kb == T::KB - 2 && !LAST) {
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
                 __syncthreads();
                 if (j + 2 < nkt) load_stage(j + 2, kbuf, vnext);
+#pragma unroll
+                for (int u = 0; u < T::KS; ++u) kcur[u] += kdelta;
+            }
+            if (kb == 1) {
+#pragma unroll
+                for (int db = 0; db < T::DB; ++db) vcur[db] += vdelta;
             }
             if (LAST) mask(kb, nk, sc[kb & 1]);
-            const char* vblk = kb > 0 ? vl + (kb - 1) * SUB : vring + vprev * T::SBYTES + (T::KB - 1) * SUB;
-            const bool next_here = kb + 2 < T::KB;
-            const char* kblk = next_here ? kl + (kb + 2) * SUB : kring + (kbuf ^ 1) * T::SBYTES + (kb + 2 - T::KB) * SUB;
             float psum[QB];
             // sub-block g-1 has the other parity
             iterate(sc[kb & 1], sc[(kb + 1) & 1], !(LAST && kb == T::KB - 1), pk[(kb + 1) & 1], pk[kb & 1], psum,
-                    vblk, kblk, next_here || !LAST);
+                    kb > 0 ? kb - 1 : T::KB - 1, (kb + 2) % T::KB, kb + 2 < T::KB || !LAST);
             if (over_limit(psum)) fix_reference(sc[kb & 1], pk[kb & 1], psum);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) l_i[qb] += psum[qb];
@@ -495,7 +488,7 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
         if (LAST) {
             // P.V of the segment's final sub-block
 #pragma unroll
-            for (int u = 0; u < T::KS; ++u) fr[u] = read_v(vl + (T::KB - 1) * SUB, u);
+            for (int u = 0; u < T::KS; ++u) fr[u] = read_v(T::KB - 1, u);
 #pragma unroll
             for (int u = 0; u < T::KS; ++u)
 #pragma unroll
@@ -515,13 +508,11 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
         // S(0), then the K fragments of sub-block 1 for the first iteration
-        {
-            bf16x8 ka[T::KS];
-            load_k(kring, 0, ka);
-            qk(ka, sc[0]);
-        }
 #pragma unroll
-        for (int u = 0; u < T::KS; ++u) fr[u] = read_k(kring + 32 * T::ROWB, u);
+        for (int u = 0; u < T::KS; ++u) fr[u] = read_k(0, u);
+        qk(fr, sc[0]);
+#pragma unroll
+        for (int u = 0; u < T::KS; ++u) fr[u] = read_k(1, u);
         // Sub-block 0 has no predecessor: its P.V slots multiply zero
         // weights with loaded (finite) V rows instead, which keeps one
         // branch-free body for every stage.
@@ -532,14 +523,16 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
                 pk[1][qb][0][e] = (__bf16)0.f;
                 pk[1][qb][1][e] = (__bf16)0.f;
             }
-        int kbuf = 0, vbuf = 0, vprev = 0, vnext = 2;  // j % 2, j % 3, (j - 1) % 3, (j + 2) % 3
+        // buffers of stage j: K j % 2, V j % 3; stage j-1's V (stage 0: its
+        // own) and stage j+2's target (j+2) % 3
+        int kbuf = 0, vbuf = 0, vprev = 0, vnext = 2;
         for (int32_t j = 0; j + 1 < nkt; ++j) {
-            stage(j, kbuf, vbuf, vprev, vnext, std::false_type{}, BN);
+            stage(j, kbuf, vnext, kbuf ? -T::SBYTES : T::SBYTES, (vbuf - vprev) * T::SBYTES, std::false_type{}, BN);
             kbuf ^= 1;
             vprev = vnext = vbuf;
             vbuf = vbuf == 2 ? 0 : vbuf + 1;
         }
-        stage(nkt - 1, kbuf, vbuf, vprev, vnext, std::true_type{}, lk - (nkt - 1) * BN);
+        stage(nkt - 1, kbuf, vnext, 0, (vbuf - vprev) * T::SBYTES, std::true_type{}, lk - (nkt - 1) * BN);
     }
 
     // ---- epilogue: O = O_acc / l (bf16), LSE = ln sum exp(scale * s) ----
