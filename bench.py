@@ -81,7 +81,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense_77k")
-    ap.add_argument("--cpu-rows", type=int, default=48, help="query rows per segment for the CPU baseline")
+    ap.add_argument("--cpu-rows", type=int, default=160, help="query rows per segment for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (scales HBM counters)")
