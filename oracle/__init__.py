@@ -28,7 +28,7 @@ _lib = None
 
 def build(force: bool = True) -> Path:
     """Compile the oracle with gcc into oracle/liboracle.so."""
-    if force or not _LIB.exists():
+    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
         tmp = _LIB.with_suffix(".so.tmp")
         cmd = ["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
                "-o", str(tmp), str(_SRC), "-lm"]
@@ -40,11 +40,11 @@ def build(force: bool = True) -> Path:
 def load_library(path) -> ctypes.CDLL:
     """ctypes handle on a compiled oracle (the default build or a test variant)."""
     lib = ctypes.CDLL(str(path))
-    f = lib.oracle_attn_varlen_fwd
-    f.restype = ctypes.c_int
-    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int32] * 3 + [ctypes.c_double,
-                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
-                  ctypes.c_int32]
+    for f in (lib.oracle_attn_varlen_fwd, lib.oracle_attn_varlen_fwd_causal):
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int32] * 3 + [ctypes.c_double,
+                      ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                      ctypes.c_int32]
     return lib
 
 
@@ -78,12 +78,14 @@ def _bits(x) -> np.ndarray:
 
 
 def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, rows=None,
-                    threads: int | None = None, library=None):
+                    threads: int | None = None, library=None, causal: bool = False):
     """fp64 attention for the given global query rows (all rows if None).
 
     q: [Nq, H, D], k/v: [Nk, H, D] bf16 (uint16 bits or CPU bf16 tensors).
     Returns (out [R, H, D] float64, lse [R, H] float64, natural log).
     `library` selects another compiled oracle (tests use it for planted mistakes).
+    causal: row r of a segment sees keys j <= r + Lk - Lq (bottom-right
+    aligned mask, the flash-attention convention; a reading, see the C file).
     """
     qb, kb, vb = _bits(q), _bits(k), _bits(v)
     if qb.ndim != 3 or kb.shape != vb.shape or kb.ndim != 3:
@@ -109,7 +111,8 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, rows=None
     if nrows == 0:
         return out, lse
     lib = library if library is not None else _load()
-    rc = lib.oracle_attn_varlen_fwd(
+    fn = lib.oracle_attn_varlen_fwd_causal if causal else lib.oracle_attn_varlen_fwd
+    rc = fn(
         qb.ctypes.data, kb.ctypes.data, vb.ctypes.data, cq.ctypes.data, ck.ctypes.data,
         B, H, D, float(scale), None if r is None else r.ctypes.data, nrows,
         out.ctypes.data, lse.ctypes.data, int(threads or default_threads()))

@@ -18,6 +18,14 @@
  *       lse   = m + ln(l)
  *   An empty key segment gives o = 0 and lse = -inf.
  *
+ *   Causal variant (oracle_attn_varlen_fwd_causal): query row r of segment b
+ *   (0-based within the segment, Lq = cu_q[b+1]-cu_q[b], Lk likewise) sees
+ *   only the keys j (0-based within the segment) with j <= r + Lk - Lq, i.e.
+ *   the mask is aligned to the bottom-right corner of the Lq x Lk score
+ *   matrix, the flash-attention convention. The pages only call the
+ *   interface with causal=False, so the alignment is a reading, not a fact
+ *   they state. A row that sees no key gives o = 0 and lse = -inf.
+ *
  * Sources: the softmax(Q K^T / sqrt(D)) V forward with its log-sum-exp that
  * the flash-attention varlen interface returns ("[FA4] cute varlen backward:
  * int32 overflow in _bwd_preprocess ..." page, "Real-world trigger" and the
@@ -57,6 +65,7 @@ typedef struct {
     double *out, *lse;
     int64_t item_begin, item_end; /* work items are (row index, head) pairs */
     int64_t max_keys;
+    int32_t causal;
     int status;
 } oracle_job;
 
@@ -82,7 +91,13 @@ static void one_row_one_head(const oracle_job *job, int64_t r, int32_t h, double
     const int32_t b = segment_of_row(job->cu_q, job->num_segments, row);
     double *o = job->out + (r * H + h) * D;
     const int64_t k0 = job->cu_k[b], k1 = job->cu_k[b + 1];
-    const int64_t nk = k1 - k0;
+    int64_t nk = k1 - k0;
+    if (job->causal) {
+        /* keys j <= (row - cu_q[b]) + Lk - Lq are visible */
+        const int64_t lq = (int64_t)job->cu_q[b + 1] - job->cu_q[b];
+        const int64_t visible = (row - job->cu_q[b]) + nk - lq + 1;
+        nk = visible < 0 ? 0 : (visible < nk ? visible : nk);
+    }
     if (nk == 0) {
         for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
         job->lse[r * H + h] = -INFINITY;
@@ -130,19 +145,10 @@ static void *run_job(void *arg) {
     return NULL;
 }
 
-/*
- * Evaluate attention for the query rows listed in `rows` (global token indices
- * into q), or for every query row when `rows` is NULL (then num_rows must be
- * cu_q[num_segments]).
- *   q: [Nq, H, D], k and v: [Nk, H, D] contiguous bf16 bit patterns.
- *   out: [num_rows, H, D] doubles; lse: [num_rows, H] doubles (natural log).
- * Returns 0 on success, -1 on bad arguments or allocation failure.
- */
-int oracle_attn_varlen_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                           const int32_t *cu_q, const int32_t *cu_k, int32_t num_segments,
-                           int32_t num_heads, int32_t head_dim, double scale,
-                           const int64_t *rows, int64_t num_rows, double *out, double *lse,
-                           int32_t num_threads) {
+static int run_all(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *cu_q,
+                   const int32_t *cu_k, int32_t num_segments, int32_t num_heads, int32_t head_dim,
+                   double scale, const int64_t *rows, int64_t num_rows, double *out, double *lse,
+                   int32_t num_threads, int32_t causal) {
     if (!cu_q || !cu_k || num_segments < 0 || num_heads <= 0 || head_dim <= 0 || num_rows < 0)
         return -1;
     if (num_rows == 0) return 0;
@@ -178,6 +184,7 @@ int oracle_attn_varlen_fwd(const uint16_t *q, const uint16_t *k, const uint16_t 
         j->item_begin = items * t / num_threads;
         j->item_end = items * (t + 1) / num_threads;
         j->max_keys = max_keys;
+        j->causal = causal;
         j->status = -1;
         if (t == 0) continue; /* the calling thread does slice 0 */
         if (pthread_create(&tids[t], NULL, run_job, j) != 0) {
@@ -193,4 +200,31 @@ int oracle_attn_varlen_fwd(const uint16_t *q, const uint16_t *k, const uint16_t 
     free(jobs);
     free(tids);
     return rc;
+}
+
+/*
+ * Evaluate attention for the query rows listed in `rows` (global token indices
+ * into q), or for every query row when `rows` is NULL (then num_rows must be
+ * cu_q[num_segments]).
+ *   q: [Nq, H, D], k and v: [Nk, H, D] contiguous bf16 bit patterns.
+ *   out: [num_rows, H, D] doubles; lse: [num_rows, H] doubles (natural log).
+ * Returns 0 on success, -1 on bad arguments or allocation failure.
+ */
+int oracle_attn_varlen_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           const int32_t *cu_q, const int32_t *cu_k, int32_t num_segments,
+                           int32_t num_heads, int32_t head_dim, double scale,
+                           const int64_t *rows, int64_t num_rows, double *out, double *lse,
+                           int32_t num_threads) {
+    return run_all(q, k, v, cu_q, cu_k, num_segments, num_heads, head_dim, scale, rows, num_rows,
+                   out, lse, num_threads, 0);
+}
+
+/* The same with the bottom-right aligned causal mask described above. */
+int oracle_attn_varlen_fwd_causal(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                  const int32_t *cu_q, const int32_t *cu_k, int32_t num_segments,
+                                  int32_t num_heads, int32_t head_dim, double scale,
+                                  const int64_t *rows, int64_t num_rows, double *out,
+                                  double *lse, int32_t num_threads) {
+    return run_all(q, k, v, cu_q, cu_k, num_segments, num_heads, head_dim, scale, rows, num_rows,
+                   out, lse, num_threads, 1);
 }

@@ -32,10 +32,13 @@ def _widen(bits: np.ndarray) -> np.ndarray:
 
 
 def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, rows=None,
-                    row_chunk: int = 128, threads: int | None = None):
+                    row_chunk: int = 128, threads: int | None = None, causal: bool = False):
     """Returns (out [R, H, D] float64, lse [R, H] float64) for the requested
     global query rows (all rows if None), in the order given. (segment, head)
-    pairs run on `threads` Python threads, each with single-threaded BLAS."""
+    pairs run on `threads` Python threads, each with single-threaded BLAS.
+    causal: row r of a segment sees keys j <= r + Lk - Lq (bottom-right
+    aligned, the same reading as the C oracle); a row that sees no key gives
+    o = 0 and lse = -inf."""
     qb, kb, vb = _bits(q), _bits(k), _bits(v)
     if qb.ndim != 3 or kb.ndim != 3 or kb.shape != vb.shape or kb.shape[1:] != qb.shape[1:]:
         raise ValueError("q must be [Nq,H,D] and k, v [Nk,H,D] with the same H, D")
@@ -64,11 +67,16 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, rows=None
             idx = sel[c0:c0 + row_chunk]
             Q = _widen(qb[rows[idx], h, :])
             S = scale * (Q @ K.T)
+            if causal:
+                last = rows[idx] - cq[b] + (ke - ks) - (cq[b + 1] - cq[b])  # last visible key
+                S = np.where(np.arange(ke - ks)[None, :] > last[:, None], -np.inf, S)
             m = S.max(axis=1, keepdims=True)
-            E = np.exp(S - m)
+            seen = np.isfinite(m[:, 0])
+            E = np.exp(S - np.where(seen[:, None], m, 0.0))
             l = E.sum(axis=1)
-            out[idx, h, :] = (E @ V) / l[:, None]
-            lse[idx, h] = m[:, 0] + np.log(l)
+            out[idx, h, :] = np.where(seen[:, None], (E @ V) / np.where(seen, l, 1.0)[:, None], 0.0)
+            with np.errstate(divide="ignore"):
+                lse[idx, h] = np.where(seen, m[:, 0] + np.log(l), -np.inf)
 
     work = [(int(b), h) for b in np.unique(seg) for h in range(H)]
     nthreads = max(1, min(int(threads or default_threads()), len(work)))

@@ -41,9 +41,11 @@ def rand_case(rng, cu_q, cu_k, H, D, std=1.0):
     return q, k, v
 
 
-def brute_force(q, k, v, cu_q, cu_k, scale):
+def brute_force(q, k, v, cu_q, cu_k, scale, causal=False):
     """Explicit score matrix in long double, softmax WITHOUT max subtraction
-    (exp(s)/sum exp(s)); valid for the small |s| used here."""
+    (exp(s)/sum exp(s)); valid for the small |s| used here. causal: a 0/1
+    visibility matrix, 1 where key j <= row r + Lk - Lq (bottom-right
+    aligned); rows with no visible key give 0 and -inf."""
     qf, kf, vf = (bits_to_f64(x).astype(np.longdouble) for x in (q, k, v))
     nq, H, D = qf.shape
     out = np.zeros((nq, H, D), dtype=np.longdouble)
@@ -59,9 +61,16 @@ def brute_force(q, k, v, cu_q, cu_k, scale):
                 continue
             S = np.longdouble(scale) * (qf[qs:qe, h] @ kf[ks:ke, h].T)
             E = np.exp(S)
+            if causal:
+                lq, lk = qe - qs, ke - ks
+                vis = np.array([[1 if j <= r + lk - lq else 0 for j in range(lk)] for r in range(lq)],
+                               dtype=np.longdouble)
+                E = E * vis
             Z = E.sum(axis=1, keepdims=True)
-            out[qs:qe, h] = (E / Z) @ vf[ks:ke, h]
-            lse[qs:qe, h] = np.log(Z[:, 0])
+            none = Z[:, 0] == 0
+            out[qs:qe, h] = np.where(none[:, None], 0, (E / np.where(none, 1, Z[:, 0])[:, None]) @ vf[ks:ke, h])
+            with np.errstate(divide="ignore"):
+                lse[qs:qe, h] = np.log(Z[:, 0])
     return out.astype(np.float64), lse.astype(np.float64)
 
 
@@ -87,15 +96,15 @@ def sdpa_reference(q, k, v, cu_q, cu_k, scale):
 
 def c_oracle(library=None):
     """The C oracle (default build, or a planted-mistake build) as a callable."""
-    def F(q, k, v, cu_q, cu_k, scale, rows=None, threads=4):
+    def F(q, k, v, cu_q, cu_k, scale, rows=None, threads=4, causal=False):
         return oracle.attn_varlen_fwd(q, k, v, cu_q, cu_k, scale, rows=rows, threads=threads,
-                                      library=library)
+                                      library=library, causal=causal)
     F.bitwise = True   # row results do not depend on which other rows are evaluated
     return F
 
 
-def blas_oracle_fn(q, k, v, cu_q, cu_k, scale, rows=None, threads=None):
-    return blas_oracle.attn_varlen_fwd(q, k, v, cu_q, cu_k, scale, rows=rows, row_chunk=3)
+def blas_oracle_fn(q, k, v, cu_q, cu_k, scale, rows=None, threads=None, causal=False):
+    return blas_oracle.attn_varlen_fwd(q, k, v, cu_q, cu_k, scale, rows=rows, row_chunk=3, causal=causal)
 
 
 # a BLAS product's rounding may depend on the operand shapes, so row results
@@ -256,7 +265,88 @@ def pin_invariants(F):
     np.testing.assert_allclose(l3, l4, rtol=1e-13, atol=1e-15)
 
 
-PINS = [pin_brute_force, pin_small_integers, pin_sdpa, pin_closed_forms, pin_needle, pin_invariants]
+# ---- causal (bottom-right aligned mask; a reading, the pages only use causal=False)
+
+CAUSAL_CASES = [([0, 6], [0, 6], 2, 8),            # square
+                ([0, 3, 9], [0, 7, 10], 2, 4),       # Lq < Lk, then Lq > Lk (rows with no key)
+                ([0, 5, 5, 7], [0, 2, 4, 4], 1, 6),  # Lq > Lk, empty Lq, empty Lk
+                ([0, 1, 4], [0, 9, 11], 2, 6)]
+
+
+def pin_causal_brute_force(F):
+    rng = np.random.default_rng(21)
+    for cu_q, cu_k, H, D in CAUSAL_CASES:
+        q, k, v = rand_case(rng, cu_q, cu_k, H, D)
+        scale = 1.0 / math.sqrt(D)
+        o, l = F(q, k, v, cu_q, cu_k, scale, causal=True)
+        bo, bl = brute_force(q, k, v, cu_q, cu_k, scale, causal=True)
+        np.testing.assert_allclose(o, bo, rtol=1e-12, atol=1e-13)
+        fin = np.isfinite(bl)
+        np.testing.assert_array_equal(np.isfinite(l), fin)
+        np.testing.assert_allclose(l[fin], bl[fin], rtol=1e-12, atol=1e-13)
+        assert np.all(l[~fin] == -np.inf) and np.all(o[~fin] == 0)
+
+
+def pin_causal_sdpa_square(F):
+    """torch's fp64 SDPA with is_causal=True (top-left aligned, which equals
+    bottom-right when Lq == Lk) on square segments."""
+    rng = np.random.default_rng(22)
+    cu = [0, 17, 17, 40]
+    q, k, v = rand_case(rng, cu, cu, 3, 16)
+    o, l = F(q, k, v, cu, cu, 0.25, causal=True)
+    qf, kf, vf = (torch.from_numpy(bits_to_f64(x)) for x in (q, k, v))
+    for b in range(len(cu) - 1):
+        s, e = cu[b], cu[b + 1]
+        if e == s:
+            continue
+        Q, K, V = (t[s:e].permute(1, 0, 2).unsqueeze(0) for t in (qf, kf, vf))
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=0.25, is_causal=True)
+        np.testing.assert_allclose(o[s:e], ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def pin_causal_prefix(F):
+    """Causal row r equals the unmasked result over the keys 0..r+Lk-Lq of its
+    segment (a one-segment run with cu_k cut there)."""
+    rng = np.random.default_rng(23)
+    cu_q, cu_k = [0, 5, 12], [0, 9, 15]
+    q, k, v = rand_case(rng, cu_q, cu_k, 2, 8)
+    o, l = F(q, k, v, cu_q, cu_k, 0.3, causal=True)
+    for b in range(2):
+        lq, lk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        for r in range(lq):
+            n = min(lk, r + lk - lq + 1)
+            row = cu_q[b] + r
+            if n <= 0:
+                assert np.all(o[row] == 0) and np.all(l[row] == -np.inf)
+                continue
+            qs = q[row:row + 1]
+            ks = k[cu_k[b]:cu_k[b] + n]
+            vs = v[cu_k[b]:cu_k[b] + n]
+            po, pl = F(qs, ks, vs, [0, 1], [0, n], 0.3)
+            np.testing.assert_allclose(o[row], po[0], rtol=1e-13, atol=1e-15)
+            np.testing.assert_allclose(l[row], pl[0], rtol=1e-13, atol=1e-15)
+
+
+def pin_causal_closed_forms(F):
+    rng = np.random.default_rng(24)
+    # square: row 0 sees only key 0 (o = v0, lse = s00); the last row sees all keys
+    cu = [0, 8]
+    q, k, v = rand_case(rng, cu, cu, 2, 8)
+    o, l = F(q, k, v, cu, cu, 0.5, causal=True)
+    on, ln = F(q, k, v, cu, cu, 0.5)
+    np.testing.assert_array_equal(o[0], bits_to_f64(v[0]))
+    s00 = 0.5 * np.sum(bits_to_f64(q[0]) * bits_to_f64(k[0]), axis=-1)
+    np.testing.assert_allclose(l[0], s00, rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(o[7], on[7], rtol=1e-14, atol=1e-15)
+    # Lq > Lk: the first Lq - Lk rows see nothing; Lq < Lk: row 0 sees Lk - Lq + 1 keys
+    q, k, v = rand_case(rng, [0, 6], [0, 2], 1, 4)
+    o, l = F(q, k, v, [0, 6], [0, 2], 1.0, causal=True)
+    assert np.all(o[:4] == 0) and np.all(l[:4] == -np.inf) and np.all(np.isfinite(l[4:]))
+    np.testing.assert_array_equal(o[4, 0], bits_to_f64(v[0, 0]))
+
+
+PINS = [pin_brute_force, pin_small_integers, pin_sdpa, pin_closed_forms, pin_needle, pin_invariants,
+        pin_causal_brute_force, pin_causal_sdpa_square, pin_causal_prefix, pin_causal_closed_forms]
 
 
 IMPLS = {"c": None, "blas": blas_oracle_fn}
@@ -286,6 +376,19 @@ def test_c_and_blas_oracles_agree():
     np.testing.assert_allclose(l1[fin], l2[fin], rtol=1e-12, atol=1e-13)
 
 
+def test_c_and_blas_oracles_agree_causal():
+    rng = np.random.default_rng(10)
+    cu_q, cu_k, H, D = [0, 130, 131, 400, 450], [0, 257, 300, 300, 420], 2, 64
+    q, k, v = rand_case(rng, cu_q, cu_k, H, D, std=1.0)
+    rows = [0, 5, 129, 130, 131, 132, 399, 250, 400, 449]
+    o1, l1 = c_oracle()(q, k, v, cu_q, cu_k, 0.1, rows=rows, causal=True)
+    o2, l2 = blas_oracle_fn(q, k, v, cu_q, cu_k, 0.1, rows=rows, causal=True)
+    np.testing.assert_allclose(o1, o2, rtol=1e-11, atol=1e-13)
+    fin = np.isfinite(l1)
+    assert np.array_equal(fin, np.isfinite(l2)) and np.all(l2[~fin] == -np.inf)
+    np.testing.assert_allclose(l1[fin], l2[fin], rtol=1e-12, atol=1e-13)
+
+
 def test_oracle_rejects_bad_arguments():
     q = to_bf16_bits(np.zeros((4, 1, 8)))
     with pytest.raises(ValueError):
@@ -306,7 +409,12 @@ MUTANTS = {
     "v_head0": ("const uint16_t *vj = job->v + ((k0 + j) * H + h) * D;",
                 "const uint16_t *vj = job->v + ((k0 + j) * H + 0) * D;"),
     "k_dim_shift": ("bf16_bits_to_double(kj[d]);", "bf16_bits_to_double(kj[(d + 1) % D]);"),
-    "drop_last_key": ("const int64_t nk = k1 - k0;", "const int64_t nk = (k1 - k0 > 1) ? k1 - k0 - 1 : k1 - k0;"),
+    "drop_last_key": ("int64_t nk = k1 - k0;", "int64_t nk = (k1 - k0 > 1) ? k1 - k0 - 1 : k1 - k0;"),
+    "causal_top_left": ("const int64_t visible = (row - job->cu_q[b]) + nk - lq + 1;",
+                        "const int64_t visible = (row - job->cu_q[b]) + 1;"),
+    "causal_off_by_one": ("const int64_t visible = (row - job->cu_q[b]) + nk - lq + 1;",
+                          "const int64_t visible = (row - job->cu_q[b]) + nk - lq;"),
+    "causal_ignored": ("nk = visible < 0 ? 0 : (visible < nk ? visible : nk);", "(void)visible;"),
     "min_not_max": ("if (scores[j] > m) m = scores[j];", "if (scores[j] < m) m = scores[j];"),
     "q_next_row": ("const uint16_t *qi = job->q + (row * H + h) * D;",
                    "const uint16_t *qi = job->q + ((row > 0 ? row - 1 : row) * H + h) * D;"),
