@@ -61,18 +61,14 @@ def cpu_baseline(w, t, rows_per_segment: int):
     rows = sample_rows(w, rows_per_segment, edge=min(8, rows_per_segment // 2))
     q, k, v = (t[n].contiguous().cpu() for n in ("q", "k", "v"))
     threads = oracle.default_threads()
-    flops = 0
-    import bisect
-    for r in rows:
-        b = bisect.bisect_right(w.cu_q, r) - 1
-        flops += 4 * (w.cu_k[b + 1] - w.cu_k[b]) * w.head_dim * w.num_heads
+    flops = sum(4 * w.visible_keys(r) * w.head_dim * w.num_heads for r in rows)
     t0 = time.perf_counter()
     oracle.attn_varlen_fwd(q, k, v, w.cu_q, w.cu_k, float(np.float32(w.softmax_scale)), rows=rows,
-                           threads=threads)
+                           threads=threads, causal=w.causal)
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(rows)} query rows x {w.num_heads} heads of {w.name} against their full key "
-                      f"segments (C fp64 oracle, {dt:.1f} s, {flops / 1e9:.1f} GFLOP)"}
+            "sample": f"{len(rows)} query rows x {w.num_heads} heads of {w.name} against their "
+                      f"{'visible ' if w.causal else ''}segments (C fp64 oracle, {dt:.1f} s, {flops / 1e9:.1f} GFLOP)"}
 
 
 def main() -> int:
@@ -118,7 +114,7 @@ def main() -> int:
 
     def step():
         avf.attn_varlen_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
-                            softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"])
+                            softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"], causal=w.causal)
 
     for _ in range(args.warmup):
         step()
@@ -143,7 +139,8 @@ def main() -> int:
         e0.record(stream)
         avf.attn_varlen_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
                             softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"],
-                            cu_seqlens_q_host=cu_q, cu_seqlens_k_host=cu_k, stream=stream.cuda_stream)
+                            cu_seqlens_q_host=cu_q, cu_seqlens_k_host=cu_k, stream=stream.cuda_stream,
+                            causal=w.causal)
         e1.record(stream)
         durs.append((e0, e1))
     torch.cuda.synchronize()
@@ -180,7 +177,7 @@ def main() -> int:
         "config": {"workload": w.name, "num_heads": w.num_heads, "head_dim": w.head_dim,
                    "segments": w.num_segments, "total_q": w.total_q, "total_k": w.total_k,
                    "max_seqlen_q": w.max_seqlen_q, "max_seqlen_k": w.max_seqlen_k,
-                   "layout": w.layout, "causal": False, "flops_per_step": flops,
+                   "layout": w.layout, "causal": w.causal, "flops_per_step": flops,
                    "workgroups": wgs, "block_m": avf.block_m(w.head_dim)},
         "roofline": roofline,
         "cpu_baseline": cpu,

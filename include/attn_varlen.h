@@ -12,7 +12,8 @@
  * ..." page ("Real-world trigger", repro script forward call) and the
  * "[FA4][SM120] flash_attn_varlen_func ... illegal memory access at >=4 varlen
  * segments" page ("Bug 2 details": packed q [35280,56,128], cu_seqlens_q,
- * max_seqlen_q/k). Non-causal; equal head counts for Q and K/V.
+ * max_seqlen_q/k). Equal head counts for Q and K/V; non-causal unless the
+ * ATTN_VARLEN_CAUSAL option (below) is given.
  *
  * Layout. q, out: [total_q, H, D]; k, v: [total_k, H, D]; bf16; the D
  * dimension is contiguous (stride 1); the token-row and head strides are free
@@ -169,6 +170,83 @@ int64_t attn_varlen_element_offset(int64_t row, int64_t row_stride, int64_t head
 
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char* attn_varlen_last_error(void);
+
+/*
+ * ---- Options: causal masking -------------------------------------------
+ *
+ * ATTN_VARLEN_CAUSAL: query row r of a segment (0-based within the segment,
+ * Lq query and Lk key rows) sees only the keys j <= r + Lk - Lq of that
+ * segment, the causal mask aligned to the bottom-right corner of the Lq x Lk
+ * score matrix as in the flash-attention interfaces. The pages call
+ * flash_attn_varlen_func with causal=False only ("[FA4] cute varlen backward:
+ * int32 overflow in _bwd_preprocess ...", repro script), so the alignment is
+ * the library's reading. A query row that sees no key (r + Lk - Lq < 0)
+ * gets O = 0 and LSE = -inf. Any other bit of `flags` is ATTN_VARLEN_EINVAL.
+ */
+#define ATTN_VARLEN_CAUSAL 1u
+
+/* attn_varlen_fwd with option flags (flags == 0 is attn_varlen_fwd). */
+int32_t attn_varlen_fwd_ex(const void* q, const void* k, const void* v,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t num_segments, int32_t num_heads, int32_t head_dim,
+                           int32_t max_seqlen_q, int32_t max_seqlen_k,
+                           const attn_varlen_layout* layout, float softmax_scale, uint32_t flags,
+                           void* out, float* lse, void* stream);
+
+/* attn_varlen_fwd_hostcu with option flags. */
+int32_t attn_varlen_fwd_hostcu_ex(const void* q, const void* k, const void* v,
+                                  const int32_t* cu_seqlens_q_host,
+                                  const int32_t* cu_seqlens_k_host, int32_t num_segments,
+                                  int32_t num_heads, int32_t head_dim, int32_t max_seqlen_q,
+                                  int32_t max_seqlen_k, const attn_varlen_layout* layout,
+                                  float softmax_scale, uint32_t flags, void* out, float* lse,
+                                  void* stream);
+
+/* attn_varlen_validate with option flags. */
+int32_t attn_varlen_validate_ex(const void* q, const void* k, const void* v,
+                                const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_k_host,
+                                int32_t num_segments, int32_t num_heads, int32_t head_dim,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                const attn_varlen_layout* layout, float softmax_scale,
+                                uint32_t flags, const void* out, const float* lse);
+
+/*
+ * ---- Batched dense form ---------------------------------------------------
+ *
+ * The batched call form flash_attn_func on [W, S, H, D] views, which the
+ * "[FA4][SM120] flash_attn_varlen_func ... illegal memory access at >=4 varlen
+ * segments" page runs next to the varlen form ("What rules things out":
+ * "varlen and batched-dense (flash_attn_func on [W, S, H, D] views)"). It is
+ * the varlen operation with W segments of seqlen_q query rows and seqlen_k
+ * key rows each; batch b of q/k/v/out is that segment.
+ *
+ * Layout (strides in ELEMENTS, D contiguous): q[b, s, h, :] at
+ * b*q_batch + s*q_row + h*q_head; k, v, out likewise; lse is fp32 [W, H, Sq]:
+ * element (b, h, s) at b*lse_batch + h*lse_head + s. Row and batch strides are
+ * multiples of 8 elements, row strides at most ATTN_VARLEN_MAX_ROW_STRIDE;
+ * out and lse must not overlap themselves; W * seqlen_q and W * seqlen_k
+ * must stay below 2^31. No cu_seqlens and no device-to-host copy: the call
+ * only enqueues work on `stream`. flags: 0 or ATTN_VARLEN_CAUSAL.
+ */
+typedef struct attn_batched_layout {
+    int64_t q_batch, q_row, q_head;
+    int64_t k_batch, k_row, k_head;
+    int64_t v_batch, v_row, v_head;
+    int64_t o_batch, o_row, o_head;
+    int64_t lse_batch, lse_head; /* lse[b*lse_batch + h*lse_head + s] */
+} attn_batched_layout;
+
+int32_t attn_fwd_batched(const void* q, const void* k, const void* v, int32_t batch,
+                         int32_t seqlen_q, int32_t seqlen_k, int32_t num_heads, int32_t head_dim,
+                         const attn_batched_layout* layout, float softmax_scale, uint32_t flags,
+                         void* out, float* lse, void* stream);
+
+/* Argument check of attn_fwd_batched without any HIP call. */
+int32_t attn_fwd_batched_validate(const void* q, const void* k, const void* v, int32_t batch,
+                                  int32_t seqlen_q, int32_t seqlen_k, int32_t num_heads,
+                                  int32_t head_dim, const attn_batched_layout* layout,
+                                  float softmax_scale, uint32_t flags, const void* out,
+                                  const float* lse);
 
 #ifdef __cplusplus
 }

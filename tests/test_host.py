@@ -30,7 +30,7 @@ def built():
 def header_functions():
     text = (ROOT / "include" / "attn_varlen.h").read_text()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_varlen_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(attn_(?:varlen|fwd)_?\w*)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -220,3 +220,58 @@ def test_forward_rejects_cpu_tensors_before_any_hip_call():
     cu = torch.tensor([0, 4], dtype=torch.int32)
     with pytest.raises(ValueError):
         avf.attn_varlen_fwd(q, q, q, cu, cu, 4, 4)
+
+
+# ------------------------------------------------------------ option flags and the batched entry
+
+def test_validate_ex_flags():
+    cq, ck = [0, 6, 10], [0, 5, 12]
+    args = (P, P, P, cq, ck, 2, 64, 6, 7, layout(), 0.125, P, P)
+    assert avf.validate(*args, flags=0) == 0
+    assert avf.validate(*args, flags=_binding.CAUSAL) == 0
+    assert avf.validate(*args, flags=2) == _binding.EINVAL
+    assert avf.validate(*args, flags=_binding.CAUSAL | 4) == _binding.EINVAL
+
+
+def blayout(W=3, Sq=5, Sk=7, H=2, D=64, **kw):
+    """Contiguous [W, S, H, D] strides and [W, H, Sq] LSE, overridable."""
+    d = dict(q_batch=Sq * H * D, q_row=H * D, q_head=D, k_batch=Sk * H * D, k_row=H * D, k_head=D,
+             v_batch=Sk * H * D, v_row=H * D, v_head=D, o_batch=Sq * H * D, o_row=H * D, o_head=D,
+             lse_batch=H * Sq, lse_head=Sq)
+    d.update(kw)
+    return avf.BatchedLayout(**d)
+
+
+def vb(W=3, Sq=5, Sk=7, H=2, D=64, lay=None, flags=0, q=P, out=P, lse=P, scale=0.125):
+    lay = lay if lay is not None else blayout(W, Sq, Sk, H, D)
+    return avf.validate_batched(q, P, P, W, Sq, Sk, H, D, lay, scale, flags, out, lse)
+
+
+def test_batched_validate_accepts():
+    assert vb() == 0
+    assert vb(flags=_binding.CAUSAL) == 0
+    assert vb(lse=None) == 0
+    assert vb(W=0) == 0 and vb(Sq=0) == 0 and vb(Sk=0) == 0
+    # [S, W, H, D] storage seen as [W, S, H, D]: batch stride H*D, row stride W*H*D
+    W, S, H, D = 4, 9, 2, 96
+    lay = blayout(W, S, S, H, D, q_batch=H * D, q_row=W * H * D, k_batch=H * D, k_row=W * H * D,
+                  v_batch=H * D, v_row=W * H * D, o_batch=H * D, o_row=W * H * D)
+    assert vb(W, S, S, H, D, lay=lay) == 0
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(W=-1), _binding.EINVAL),
+    (dict(Sq=-2), _binding.EINVAL),
+    (dict(flags=8), _binding.EINVAL),
+    (dict(q=None), _binding.ENULL),
+    (dict(q=P + 4), _binding.EALIGN),
+    (dict(lay=blayout(q_batch=5 * 2 * 64 + 4)), _binding.EALIGN),   # batch stride not a multiple of 8
+    (dict(lay=blayout(k_batch=-128)), _binding.EINVAL),
+    (dict(lay=blayout(o_batch=4 * 2 * 64)), _binding.EINVAL),       # out batches overlap
+    (dict(lay=blayout(lse_batch=5)), _binding.EINVAL),              # lse batches overlap
+    (dict(lay=blayout(lse_head=3)), _binding.EINVAL),               # lse heads overlap
+    (dict(W=1 << 20, Sq=1 << 12), _binding.EUNSUPPORTED),           # W * Sq >= 2^31
+    (dict(D=80, lay=blayout(D=80)), _binding.EUNSUPPORTED),
+])
+def test_batched_validate_rejects(kwargs, code):
+    assert vb(**kwargs) == code

@@ -24,7 +24,11 @@ EXPORTED_SYMBOLS = (
     "attn_varlen_fwd", "attn_varlen_fwd_hostcu", "attn_varlen_validate", "attn_varlen_block_m",
     "attn_varlen_count_tiles", "attn_varlen_grid_plan", "attn_varlen_segments_per_launch",
     "attn_varlen_decode_tile", "attn_varlen_element_offset", "attn_varlen_last_error",
+    "attn_varlen_fwd_ex", "attn_varlen_fwd_hostcu_ex", "attn_varlen_validate_ex",
+    "attn_fwd_batched", "attn_fwd_batched_validate",
 )
+
+CAUSAL = 1  # ATTN_VARLEN_CAUSAL
 
 
 class AttnVarlenError(RuntimeError):
@@ -37,6 +41,12 @@ class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "q_row", "q_head", "k_row", "k_head", "v_row", "v_head", "o_row", "o_head",
         "lse_head", "q_tokens", "k_tokens")]
+
+
+class BatchedLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "q_batch", "q_row", "q_head", "k_batch", "k_row", "k_head", "v_batch", "v_row", "v_head",
+        "o_batch", "o_row", "o_head", "lse_batch", "lse_head")]
 
 
 _lib = None
@@ -62,6 +72,19 @@ def lib():
             f.argtypes = fwd_args
         L.attn_varlen_validate.restype = ctypes.c_int32
         L.attn_varlen_validate.argtypes = fwd_args[:-1]
+        ex_args = fwd_args[:12] + [ctypes.c_uint32] + fwd_args[12:]
+        for name in ("attn_varlen_fwd_ex", "attn_varlen_fwd_hostcu_ex"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int32
+            f.argtypes = ex_args
+        L.attn_varlen_validate_ex.restype = ctypes.c_int32
+        L.attn_varlen_validate_ex.argtypes = ex_args[:-1]
+        b_args = [_vp, _vp, _vp] + [ctypes.c_int32] * 5 + [ctypes.POINTER(BatchedLayout), ctypes.c_float,
+                                                          ctypes.c_uint32, _vp, _vp, _vp]
+        L.attn_fwd_batched.restype = ctypes.c_int32
+        L.attn_fwd_batched.argtypes = b_args
+        L.attn_fwd_batched_validate.restype = ctypes.c_int32
+        L.attn_fwd_batched_validate.argtypes = b_args[:-1]
         L.attn_varlen_block_m.restype = ctypes.c_int32
         L.attn_varlen_block_m.argtypes = [ctypes.c_int32]
         L.attn_varlen_count_tiles.restype = ctypes.c_int64
@@ -135,14 +158,25 @@ def element_offset(row: int, row_stride: int, head: int, head_stride: int) -> in
 
 
 def validate(q_ptr, k_ptr, v_ptr, cu_q, cu_k, num_heads, head_dim, max_q, max_k, layout: Layout,
-             scale: float, out_ptr, lse_ptr) -> int:
-    """Return code of the host-side argument check (no HIP call)."""
+             scale: float, out_ptr, lse_ptr, flags: int | None = None) -> int:
+    """Return code of the host-side argument check (no HIP call); flags=None
+    uses the flag-less entry point."""
     cq, B = _cu_array(cu_q)
     ck, Bk = _cu_array(cu_k)
     if Bk != B:
         raise ValueError("cu_q and cu_k differ in length")
-    return lib().attn_varlen_validate(q_ptr, k_ptr, v_ptr, cq, ck, B, num_heads, head_dim, max_q,
-                                      max_k, ctypes.byref(layout), scale, out_ptr, lse_ptr)
+    if flags is None:
+        return lib().attn_varlen_validate(q_ptr, k_ptr, v_ptr, cq, ck, B, num_heads, head_dim, max_q,
+                                          max_k, ctypes.byref(layout), scale, out_ptr, lse_ptr)
+    return lib().attn_varlen_validate_ex(q_ptr, k_ptr, v_ptr, cq, ck, B, num_heads, head_dim, max_q,
+                                         max_k, ctypes.byref(layout), scale, flags, out_ptr, lse_ptr)
+
+
+def validate_batched(q_ptr, k_ptr, v_ptr, batch, seqlen_q, seqlen_k, num_heads, head_dim,
+                     layout: BatchedLayout, scale: float, flags: int, out_ptr, lse_ptr) -> int:
+    """Return code of the batched entry point's argument check (no HIP call)."""
+    return lib().attn_fwd_batched_validate(q_ptr, k_ptr, v_ptr, batch, seqlen_q, seqlen_k, num_heads,
+                                           head_dim, ctypes.byref(layout), scale, flags, out_ptr, lse_ptr)
 
 
 # ---- torch front end ----------------------------------------------------------------
@@ -157,13 +191,14 @@ def _layout_of(q, k, v, out, lse, lse_head):
 
 def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                     softmax_scale: float | None = None, out=None, lse=None, return_lse: bool = True,
-                    cu_seqlens_q_host=None, cu_seqlens_k_host=None, stream=None):
+                    cu_seqlens_q_host=None, cu_seqlens_k_host=None, stream=None, causal: bool = False):
     """Varlen attention forward on torch's current stream.
 
     q: [total_q, H, D], k/v: [total_k, H, D] bf16 CUDA tensors (any token and
     head strides, contiguous D). cu_seqlens_q/k: int32 CUDA tensors [B+1].
     When host copies of cu_seqlens are given, the synchronisation-free entry
-    point is used. Returns (out [total_q, H, D] bf16, lse [H, total_q] fp32 or None).
+    point is used. causal: row r of a segment sees keys j <= r + Lk - Lq.
+    Returns (out [total_q, H, D] bf16, lse [H, total_q] fp32 or None).
     """
     import torch
 
@@ -198,9 +233,10 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
         ck, Bk = _cu_array(cu_seqlens_k_host)
         if B != Bk:
             raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
-        rc = L.attn_varlen_fwd_hostcu(q.data_ptr(), k.data_ptr(), v.data_ptr(), cq, ck, B, H, D,
-                                      int(max_seqlen_q), int(max_seqlen_k), ctypes.byref(layout),
-                                      float(softmax_scale), out.data_ptr(), lse_ptr, stream)
+        rc = L.attn_varlen_fwd_hostcu_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), cq, ck, B, H, D,
+                                         int(max_seqlen_q), int(max_seqlen_k), ctypes.byref(layout),
+                                         float(softmax_scale), CAUSAL if causal else 0, out.data_ptr(),
+                                         lse_ptr, stream)
     else:
         for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
             if cu.dtype != torch.int32 or not cu.is_cuda or cu.dim() != 1 or not cu.is_contiguous():
@@ -208,8 +244,55 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
         B = cu_seqlens_q.numel() - 1
         if cu_seqlens_k.numel() != B + 1:
             raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
-        rc = L.attn_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
-                               cu_seqlens_k.data_ptr(), B, H, D, int(max_seqlen_q), int(max_seqlen_k),
-                               ctypes.byref(layout), float(softmax_scale), out.data_ptr(), lse_ptr, stream)
+        rc = L.attn_varlen_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
+                                  cu_seqlens_k.data_ptr(), B, H, D, int(max_seqlen_q), int(max_seqlen_k),
+                                  ctypes.byref(layout), float(softmax_scale), CAUSAL if causal else 0,
+                                  out.data_ptr(), lse_ptr, stream)
+    _check(rc)
+    return out, lse
+
+
+def attn_fwd(q, k, v, softmax_scale: float | None = None, causal: bool = False, out=None, lse=None,
+             return_lse: bool = True, stream=None):
+    """Batched dense attention forward (the flash_attn_func form) on torch's
+    current stream: q [W, Sq, H, D], k/v [W, Sk, H, D] bf16 CUDA tensors with
+    any batch, row and head strides and a contiguous D. Returns
+    (out [W, Sq, H, D] bf16, lse [W, H, Sq] fp32 or None)."""
+    import torch
+
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [W, Sq, H, D] and k, v [W, Sk, H, D]")
+    W, Sq, H, D = q.shape
+    if k.shape[0] != W or k.shape[2:] != (H, D):
+        raise ValueError("k and v must match q's batch, head count and head dim")
+    Sk = k.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((W, Sq, H, D), dtype=torch.bfloat16, device=q.device)
+    elif out.dtype != torch.bfloat16 or out.shape != q.shape:
+        raise ValueError("out must be bf16 with q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((W, H, Sq), dtype=torch.float32, device=q.device)
+    lse_batch = lse_head = 0
+    if lse is not None:
+        if lse.dtype != torch.float32 or lse.shape != (W, H, Sq) or lse.stride(2) != 1:
+            raise ValueError("lse must be fp32 [W, H, Sq] with unit inner stride")
+        lse_batch, lse_head = lse.stride(0), lse.stride(1)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.stride(3) != 1:
+            raise ValueError(f"{name} must have a contiguous D dimension")
+    layout = BatchedLayout(q.stride(0), q.stride(1), q.stride(2), k.stride(0), k.stride(1), k.stride(2),
+                           v.stride(0), v.stride(1), v.stride(2), out.stride(0), out.stride(1), out.stride(2),
+                           lse_batch, lse_head)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().attn_fwd_batched(q.data_ptr(), k.data_ptr(), v.data_ptr(), W, Sq, Sk, H, D, ctypes.byref(layout),
+                                float(softmax_scale), CAUSAL if causal else 0, out.data_ptr(),
+                                lse.data_ptr() if lse is not None else None, stream)
     _check(rc)
     return out, lse

@@ -32,16 +32,13 @@ int32_t fail(int32_t code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// (extent, stride) pairs of a tensor whose innermost dimension is D with
-// stride 1: true if no two elements share an address (each stride, in
-// increasing order, spans everything below it).
-bool non_overlapping(int64_t rows, int64_t row_stride, int64_t heads, int64_t head_stride,
-                     int64_t d) {
-    struct Dim { int64_t extent, stride; };
+// (extent, stride) pairs of a tensor: true if no two elements share an
+// address (each stride, in increasing order, spans everything below it).
+struct Dim { int64_t extent, stride; };
+bool non_overlapping_dims(std::vector<Dim> in) {
     std::vector<Dim> dims;
-    dims.push_back({d, 1});
-    if (rows > 1) dims.push_back({rows, row_stride});
-    if (heads > 1) dims.push_back({heads, head_stride});
+    for (const Dim& x : in)
+        if (x.extent > 1) dims.push_back(x);
     std::sort(dims.begin(), dims.end(), [](const Dim& x, const Dim& y) { return x.stride < y.stride; });
     for (size_t i = 1; i < dims.size(); ++i) {
         const __int128 span = (__int128)dims[i - 1].extent * dims[i - 1].stride;
@@ -49,6 +46,22 @@ bool non_overlapping(int64_t rows, int64_t row_stride, int64_t heads, int64_t he
     }
     return true;
 }
+// [rows, heads, d] with the innermost dimension contiguous
+bool non_overlapping(int64_t rows, int64_t row_stride, int64_t heads, int64_t head_stride,
+                     int64_t d) {
+    return non_overlapping_dims({{d, 1}, {rows, row_stride}, {heads, head_stride}});
+}
+
+int32_t check_flags(uint32_t flags) {
+    if (flags & ~ATTN_VARLEN_CAUSAL)
+        return fail(ATTN_VARLEN_EINVAL, "unknown option flags 0x%x", (unsigned)(flags & ~ATTN_VARLEN_CAUSAL));
+    return ATTN_VARLEN_OK;
+}
+
+// Per-segment base offsets of batched tensors (all zero for varlen ones).
+struct SegStrides {
+    int64_t q, k, v, o, lse;
+};
 
 int32_t check_scalars(const void* q, const void* k, const void* v, int32_t B, int32_t H,
                       int32_t D, int32_t max_q, int32_t max_k, const attn_varlen_layout* st,
@@ -174,7 +187,7 @@ constexpr int64_t kMaxTilesPerLaunch = (int64_t)1 << 23;
 
 int32_t run(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
             int32_t B, int32_t H, int32_t D, const attn_varlen_layout* st, float scale, void* out,
-            float* lse, hipStream_t stream) {
+            float* lse, hipStream_t stream, uint32_t flags, const SegStrides& seg) {
     const int32_t bm = avf_block_m(D);
     AvfLaunchArgs a;
     std::memset(&a, 0, sizeof a);
@@ -187,6 +200,8 @@ int32_t run(const void* q, const void* k, const void* v, const int32_t* cu_q, co
     a.scale = scale;
     a.scale_log2e = scale * 1.4426950408889634f;
     a.num_heads = H;
+    a.causal = (flags & ATTN_VARLEN_CAUSAL) ? 1 : 0;
+    a.q_seg = seg.q; a.k_seg = seg.k; a.v_seg = seg.v; a.o_seg = seg.o; a.lse_seg = seg.lse;
     for (int32_t b0 = 0; b0 < B;) {
         // segments of this launch: at most AVF_SEGS_PER_LAUNCH and at most kMaxTilesPerLaunch tiles
         int32_t b1 = b0;
@@ -201,6 +216,7 @@ int32_t run(const void* q, const void* k, const void* v, const int32_t* cu_q, co
             ++b1;
         }
         const int64_t tiles = fill_plan(a, cu_q, cu_k, b0, b1, H, bm);
+        a.seg0 = b0;
         if (tiles > 0) {
             const hipError_t e = avf_launch(a, D, stream);
             if (e != hipSuccess)
@@ -215,30 +231,52 @@ int32_t run(const void* q, const void* k, const void* v, const int32_t* cu_q, co
 
 extern "C" {
 
+int32_t attn_varlen_validate_ex(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                                const int32_t* cu_k, int32_t B, int32_t H, int32_t D, int32_t max_q,
+                                int32_t max_k, const attn_varlen_layout* st, float scale,
+                                uint32_t flags, const void* out, const float* lse) {
+    g_last_error.clear();
+    const int32_t rc = check_flags(flags);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    return validate_all(q, k, v, cu_q, cu_k, B, H, D, max_q, max_k, st, scale, out, lse);
+}
+
 int32_t attn_varlen_validate(const void* q, const void* k, const void* v, const int32_t* cu_q,
                              const int32_t* cu_k, int32_t B, int32_t H, int32_t D, int32_t max_q,
                              int32_t max_k, const attn_varlen_layout* st, float scale,
                              const void* out, const float* lse) {
+    return attn_varlen_validate_ex(q, k, v, cu_q, cu_k, B, H, D, max_q, max_k, st, scale, 0u, out, lse);
+}
+
+int32_t attn_varlen_fwd_hostcu_ex(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                                  const int32_t* cu_k, int32_t B, int32_t H, int32_t D, int32_t max_q,
+                                  int32_t max_k, const attn_varlen_layout* st, float scale, uint32_t flags,
+                                  void* out, float* lse, void* stream) {
     g_last_error.clear();
-    return validate_all(q, k, v, cu_q, cu_k, B, H, D, max_q, max_k, st, scale, out, lse);
+    int32_t rc = check_flags(flags);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    rc = validate_all(q, k, v, cu_q, cu_k, B, H, D, max_q, max_k, st, scale, out, lse);
+    if (rc != ATTN_VARLEN_OK || B == 0) return rc;
+    return run(q, k, v, cu_q, cu_k, B, H, D, st, scale, out, lse, static_cast<hipStream_t>(stream), flags,
+               SegStrides{0, 0, 0, 0, 0});
 }
 
 int32_t attn_varlen_fwd_hostcu(const void* q, const void* k, const void* v, const int32_t* cu_q,
                                const int32_t* cu_k, int32_t B, int32_t H, int32_t D, int32_t max_q,
                                int32_t max_k, const attn_varlen_layout* st, float scale, void* out,
                                float* lse, void* stream) {
-    g_last_error.clear();
-    const int32_t rc = validate_all(q, k, v, cu_q, cu_k, B, H, D, max_q, max_k, st, scale, out, lse);
-    if (rc != ATTN_VARLEN_OK || B == 0) return rc;
-    return run(q, k, v, cu_q, cu_k, B, H, D, st, scale, out, lse, static_cast<hipStream_t>(stream));
+    return attn_varlen_fwd_hostcu_ex(q, k, v, cu_q, cu_k, B, H, D, max_q, max_k, st, scale, 0u, out, lse,
+                                     stream);
 }
 
-int32_t attn_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_q_dev,
-                        const int32_t* cu_k_dev, int32_t B, int32_t H, int32_t D, int32_t max_q,
-                        int32_t max_k, const attn_varlen_layout* st, float scale, void* out,
-                        float* lse, void* stream) {
+int32_t attn_varlen_fwd_ex(const void* q, const void* k, const void* v, const int32_t* cu_q_dev,
+                           const int32_t* cu_k_dev, int32_t B, int32_t H, int32_t D, int32_t max_q,
+                           int32_t max_k, const attn_varlen_layout* st, float scale, uint32_t flags,
+                           void* out, float* lse, void* stream) {
     g_last_error.clear();
-    int32_t rc = check_scalars(q, k, v, B, H, D, max_q, max_k, st, scale, out, lse);
+    int32_t rc = check_flags(flags);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    rc = check_scalars(q, k, v, B, H, D, max_q, max_k, st, scale, out, lse);
     if (rc != ATTN_VARLEN_OK || B == 0) return rc;
     if (!cu_q_dev || !cu_k_dev) return fail(ATTN_VARLEN_ENULL, "cu_seqlens_q/k must be non-NULL");
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -254,7 +292,96 @@ int32_t attn_varlen_fwd(const void* q, const void* k, const void* v, const int32
     if (rc != ATTN_VARLEN_OK) return rc;
     rc = check_with_cu(cq, B, H, D, st, lse);
     if (rc != ATTN_VARLEN_OK) return rc;
-    return run(q, k, v, cq, ck, B, H, D, st, scale, out, lse, s);
+    return run(q, k, v, cq, ck, B, H, D, st, scale, out, lse, s, flags, SegStrides{0, 0, 0, 0, 0});
+}
+
+int32_t attn_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_q_dev,
+                        const int32_t* cu_k_dev, int32_t B, int32_t H, int32_t D, int32_t max_q,
+                        int32_t max_k, const attn_varlen_layout* st, float scale, void* out,
+                        float* lse, void* stream) {
+    return attn_varlen_fwd_ex(q, k, v, cu_q_dev, cu_k_dev, B, H, D, max_q, max_k, st, scale, 0u, out, lse,
+                              stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Batched [W, S, H, D] tensors as W uniform segments: the varlen layout with
+// the row and head strides, host cu_seqlens b*S, and per-segment base offsets
+// that move segment b's token rows from b*S*row to b*batch.
+int32_t batched_plan(const void* q, const void* k, const void* v, int32_t W, int32_t Sq, int32_t Sk,
+                     int32_t H, int32_t D, const attn_batched_layout* bl, float scale, uint32_t flags,
+                     const void* out, const float* lse, attn_varlen_layout* st, SegStrides* seg,
+                     std::vector<int32_t>* cu_q, std::vector<int32_t>* cu_k) {
+    int32_t rc = check_flags(flags);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    if (!bl) return fail(ATTN_VARLEN_ENULL, "layout is NULL");
+    if (W < 0 || Sq < 0 || Sk < 0)
+        return fail(ATTN_VARLEN_EINVAL, "batch, seqlen_q and seqlen_k must be >= 0 (got %d, %d, %d)", W, Sq, Sk);
+    if ((int64_t)W * Sq > INT32_MAX || (int64_t)W * Sk > INT32_MAX)
+        return fail(ATTN_VARLEN_EUNSUPPORTED, "batch * seqlen must stay below 2^31");
+    const int64_t batch[4] = {bl->q_batch, bl->k_batch, bl->v_batch, bl->o_batch};
+    for (int i = 0; i < 4; ++i) {
+        if (batch[i] < 0) return fail(ATTN_VARLEN_EINVAL, "batch strides must be >= 0");
+        if (batch[i] & 7) return fail(ATTN_VARLEN_EALIGN, "batch strides must be multiples of 8 elements");
+    }
+    std::memset(st, 0, sizeof *st);
+    st->q_row = bl->q_row; st->q_head = bl->q_head;
+    st->k_row = bl->k_row; st->k_head = bl->k_head;
+    st->v_row = bl->v_row; st->v_head = bl->v_head;
+    st->o_row = bl->o_row; st->o_head = bl->o_head;
+    st->q_tokens = (int64_t)W * Sq;
+    st->k_tokens = (int64_t)W * Sk;
+    st->lse_head = bl->lse_head;
+    rc = check_scalars(q, k, v, W, H, D, Sq, Sk, st, scale, out, lse);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    if (!non_overlapping_dims({{D, 1}, {Sq, bl->o_row}, {H, bl->o_head}, {W, bl->o_batch}}))
+        return fail(ATTN_VARLEN_EINVAL, "out strides make elements overlap");
+    if (lse) {
+        if (bl->lse_head < 0 || bl->lse_batch < 0) return fail(ATTN_VARLEN_EINVAL, "lse strides must be >= 0");
+        if (!non_overlapping_dims({{Sq, 1}, {H, bl->lse_head}, {W, bl->lse_batch}}))
+            return fail(ATTN_VARLEN_EINVAL, "lse strides make elements overlap");
+    }
+    seg->q = bl->q_batch - (int64_t)Sq * bl->q_row;
+    seg->k = bl->k_batch - (int64_t)Sk * bl->k_row;
+    seg->v = bl->v_batch - (int64_t)Sk * bl->v_row;
+    seg->o = bl->o_batch - (int64_t)Sq * bl->o_row;
+    seg->lse = bl->lse_batch - Sq;
+    cu_q->resize((size_t)W + 1);
+    cu_k->resize((size_t)W + 1);
+    for (int32_t b = 0; b <= W; ++b) {
+        (*cu_q)[b] = b * Sq;
+        (*cu_k)[b] = b * Sk;
+    }
+    return ATTN_VARLEN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t attn_fwd_batched_validate(const void* q, const void* k, const void* v, int32_t W, int32_t Sq,
+                                  int32_t Sk, int32_t H, int32_t D, const attn_batched_layout* bl,
+                                  float scale, uint32_t flags, const void* out, const float* lse) {
+    g_last_error.clear();
+    attn_varlen_layout st;
+    SegStrides seg;
+    std::vector<int32_t> cq, ck;
+    return batched_plan(q, k, v, W, Sq, Sk, H, D, bl, scale, flags, out, lse, &st, &seg, &cq, &ck);
+}
+
+int32_t attn_fwd_batched(const void* q, const void* k, const void* v, int32_t W, int32_t Sq, int32_t Sk,
+                         int32_t H, int32_t D, const attn_batched_layout* bl, float scale, uint32_t flags,
+                         void* out, float* lse, void* stream) {
+    g_last_error.clear();
+    attn_varlen_layout st;
+    SegStrides seg;
+    std::vector<int32_t> cq, ck;
+    const int32_t rc = batched_plan(q, k, v, W, Sq, Sk, H, D, bl, scale, flags, out, lse, &st, &seg, &cq, &ck);
+    if (rc != ATTN_VARLEN_OK || W == 0 || Sq == 0) return rc;
+    return run(q, k, v, cq.data(), ck.data(), W, H, D, &st, scale, out, lse, static_cast<hipStream_t>(stream),
+               flags, seg);
 }
 
 int32_t attn_varlen_block_m(int32_t head_dim) {

@@ -152,7 +152,9 @@ struct Tile {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS rings");
 };
 
-template <int D, int QB, int NW, int BN>
+// CAUSAL (compile-time): apply the causal mask. A separate instantiation, so
+// the unmasked kernel carries none of its per-row limits or extra stage loop.
+template <int D, int QB, int NW, int BN, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs a) {
     using T = Tile<D, QB, NW, BN>;
     constexpr int BM = T::BM;
@@ -173,14 +175,25 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     const int32_t h = tile.head;
     const int32_t lq = a.q_start[seg + 1] - a.q_start[seg];
     const int32_t lk = a.k_start[seg + 1] - a.k_start[seg];
-    const int32_t row0 = tile.mblk * BM;
+    // Causal: later query blocks see more keys, so they are dispatched first
+    // (the block order within a (segment, head) is reversed).
+    const int32_t mblk = CAUSAL ? (lq + BM - 1) / BM - 1 - tile.mblk : tile.mblk;
+    const int32_t row0 = mblk * BM;
     const int32_t rows_here = min(BM, lq - row0);
     const int64_t q_tok0 = (int64_t)a.q_start[seg] + row0;
     const int64_t k_tok0 = (int64_t)a.k_start[seg];
+    const int64_t gseg = (int64_t)a.seg0 + seg;  // batched tensors: per-segment base offsets
+    // Keys the tile needs: all of the segment, or with the causal mask (row r
+    // sees keys j <= r + lk - lq) those up to its last row's limit. Keys below
+    // kfull are visible to every row of the tile, so only stages from
+    // kfull / BN on need the per-row mask.
+    const int32_t coff = lk - lq;
+    const int32_t k_end = CAUSAL ? max(0, min(lk, row0 + rows_here + coff)) : lk;
+    const int32_t kfull = CAUSAL ? max(0, min(k_end, row0 + 1 + coff)) : k_end;
 
     // ---- Q^T fragments (B operand), resident for the whole tile ----
     const uint32_t q_rs = (uint32_t)(a.q_row * 2);
-    const char* qptr = (const char*)a.q + 2 * avf_elem_offset(q_tok0, a.q_row, h, a.q_head);
+    const char* qptr = (const char*)a.q + 2 * (avf_elem_offset(q_tok0, a.q_row, h, a.q_head) + gseg * a.q_seg);
     const auto qrs = make_rsrc(qptr, (uint32_t)(rows_here - 1) * q_rs + 2 * D);
     const int wrow0 = wave * QB * 32;
     bf16x8 qf[QB][T::KS];
@@ -217,14 +230,15 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     // is chunk `slot` of row `key` of the stage, so it fetches chunk
     // slot ^ swz(key) of that key's row. Rows past the segment end re-read its
     // last row (finite data; they are masked out of the softmax).
-    const int32_t nkt = (lk + BN - 1) / BN;
+    const int32_t nkt = (k_end + BN - 1) / BN;
+    const int32_t jmask = kfull / BN;  // first stage that needs the per-row causal mask
     const uint32_t k_rs = (uint32_t)(a.k_row * 2);
     const uint32_t v_rs = (uint32_t)(a.v_row * 2);
     auto load_stage = [&](int32_t j, int kbuf, int vbuf) {
         const int32_t key0 = j * BN;
-        const int32_t nk = min(BN, lk - key0);
-        const char* kp = (const char*)a.k + 2 * avf_elem_offset(k_tok0 + key0, a.k_row, h, a.k_head);
-        const char* vp = (const char*)a.v + 2 * avf_elem_offset(k_tok0 + key0, a.v_row, h, a.v_head);
+        const int32_t nk = min(BN, k_end - key0);
+        const char* kp = (const char*)a.k + 2 * (avf_elem_offset(k_tok0 + key0, a.k_row, h, a.k_head) + gseg * a.k_seg);
+        const char* vp = (const char*)a.v + 2 * (avf_elem_offset(k_tok0 + key0, a.v_row, h, a.v_head) + gseg * a.v_seg);
         const i32x4 krs = rsrc_words(kp, (uint32_t)(nk - 1) * k_rs + 2 * D);
         const i32x4 vrs = rsrc_words(vp, (uint32_t)(nk - 1) * v_rs + 2 * D);
         const uint32_t kl = lds_addr + kbuf * T::SBYTES;
@@ -282,14 +296,15 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
             for (int qb = 0; qb < QB; ++qb)
                 sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[qb][ks], sc[qb], 0, 0, 0);
     };
-    // keys at or past nk (segment end) get -inf; element e of a lane holds key
-    // kb*32 + 8*(e/4) + 4*hf + e%4
-    auto mask = [&](int kb, int32_t nk, f32x16 (&sc)[QB]) {
+    // keys of the stage at or past the lane's limit lim[qb] (the segment or
+    // tile end, or the row's causal limit) get -inf; element e of a lane
+    // holds key kb*32 + 8*(e/4) + 4*hf + e%4 of the stage
+    auto mask = [&](int kb, const int32_t (&lim)[QB], f32x16 (&sc)[QB]) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const bool dead = kb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3) >= nk;
+            const int key = kb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) sc[qb][e] = dead ? -INFINITY : sc[qb][e];
+            for (int qb = 0; qb < QB; ++qb) sc[qb][e] = key >= lim[qb] ? -INFINITY : sc[qb][e];
         }
     };
     // Online softmax against a lazily moved reference m_i: the weights are
@@ -329,14 +344,18 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
 #pragma unroll
             for (int e = 1; e < 16; ++e) v = fmaxf(v, sc[qb][e]);
             const float mnew = fmaxf(m_i[qb], fmaxf(v, __shfl_xor(v, 32)));
-            const float alpha = __builtin_amdgcn_exp2f((m_i[qb] - mnew) * c);
+            // a row that has seen no key yet (every score -inf, causal rows
+            // above the diagonal) keeps m = -inf, l = 0, O = 0 and gets
+            // weights exp2(-inf) = 0 from the finite offset 0
+            const bool none = CAUSAL && mnew == -INFINITY;
+            const float alpha = none ? 1.f : __builtin_amdgcn_exp2f((m_i[qb] - mnew) * c);
             l_i[qb] *= alpha;
 #pragma unroll
             for (int db = 0; db < T::DB; ++db)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
             m_i[qb] = mnew;
-            mc_i[qb] = mnew * c;
+            mc_i[qb] = none ? 0.f : mnew * c;
         }
         weights(sc, pk, psum);
     };
@@ -461,8 +480,20 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     // buffer stage j+2 is loaded into. At the barrier the K reads move on to
     // stage j+1's buffer (kcur += kdelta); at sub-block 1 the V reads move
     // from stage j-1's buffer to stage j's (vcur += vdelta).
-    auto stage = [&](int32_t j, int kbuf, int vnext, int kdelta, int vdelta, auto last, int32_t nk) {
+    // `masked` (compile-time) applies the per-row key limit: the last stage
+    // (segment or tile end) and, with the causal mask, the stages that cross
+    // the tile's diagonal.
+    auto stage = [&](int32_t j, int kbuf, int vnext, int kdelta, int vdelta, auto last, auto masked) {
         constexpr bool LAST = decltype(last)::value;
+        constexpr bool MASKED = decltype(masked)::value || LAST;
+        int32_t lim[QB];
+        if (MASKED) {
+            const int32_t key0 = j * BN;
+            const int32_t nk = LAST ? k_end - key0 : BN;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                lim[qb] = CAUSAL ? min(nk, row0 + wrow0 + qb * 32 + l32 + coff + 1 - key0) : nk;
+        }
 #pragma unroll
         for (int kb = 0; kb < T::KB; ++kb) {
             if (kb == T::KB - 2 && !LAST) {
@@ -476,7 +507,7 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
 #pragma unroll
                 for (int db = 0; db < T::DB; ++db) vcur[db] += vdelta;
             }
-            if (LAST) mask(kb, nk, sc[kb & 1]);
+            if (MASKED) mask(kb, lim, sc[kb & 1]);
             float psum[QB];
             // sub-block g-1 has the other parity
             iterate(sc[kb & 1], sc[(kb + 1) & 1], !(LAST && kb == T::KB - 1), pk[(kb + 1) & 1], pk[kb & 1], psum,
@@ -526,18 +557,32 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
         // buffers of stage j: K j % 2, V j % 3; stage j-1's V (stage 0: its
         // own) and stage j+2's target (j+2) % 3
         int kbuf = 0, vbuf = 0, vprev = 0, vnext = 2;
-        for (int32_t j = 0; j + 1 < nkt; ++j) {
-            stage(j, kbuf, vnext, kbuf ? -T::SBYTES : T::SBYTES, (vbuf - vprev) * T::SBYTES, std::false_type{}, BN);
+        auto advance = [&]() {
             kbuf ^= 1;
             vprev = vnext = vbuf;
             vbuf = vbuf == 2 ? 0 : vbuf + 1;
+        };
+        // stages every row sees whole, then the ones crossing the causal diagonal
+        const int32_t nfree = min(jmask, nkt - 1);
+        int32_t j = 0;
+        for (; j < nfree; ++j) {
+            stage(j, kbuf, vnext, kbuf ? -T::SBYTES : T::SBYTES, (vbuf - vprev) * T::SBYTES, std::false_type{},
+                  std::false_type{});
+            advance();
         }
-        stage(nkt - 1, kbuf, vnext, 0, (vbuf - vprev) * T::SBYTES, std::true_type{}, lk - (nkt - 1) * BN);
+        if constexpr (CAUSAL) {
+            for (; j + 1 < nkt; ++j) {
+                stage(j, kbuf, vnext, kbuf ? -T::SBYTES : T::SBYTES, (vbuf - vprev) * T::SBYTES, std::false_type{},
+                      std::true_type{});
+                advance();
+            }
+        }
+        stage(nkt - 1, kbuf, vnext, 0, (vbuf - vprev) * T::SBYTES, std::true_type{}, std::true_type{});
     }
 
     // ---- epilogue: O = O_acc / l (bf16), LSE = ln sum exp(scale * s) ----
     const uint32_t o_rs = (uint32_t)(a.o_row * 2);
-    char* optr = (char*)a.o + 2 * avf_elem_offset(q_tok0, a.o_row, h, a.o_head);
+    char* optr = (char*)a.o + 2 * (avf_elem_offset(q_tok0, a.o_row, h, a.o_head) + gseg * a.o_seg);
     const auto ors = make_rsrc(optr, (uint32_t)(rows_here - 1) * o_rs + 2 * D);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -558,7 +603,7 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
             if (hf == 0 && a.lse != nullptr) {
                 // natural-log LSE: m*scale + ln l (any reference m gives the same value)
                 const float lse = l_tot > 0.f ? m_i[qb] * a.scale + __logf(l_tot) : -INFINITY;
-                a.lse[(int64_t)h * a.lse_head + q_tok0 + row] = lse;
+                a.lse[(int64_t)h * a.lse_head + q_tok0 + row + gseg * a.lse_seg] = lse;
             }
         }
     }
@@ -566,7 +611,12 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
 
 template <int D, int QB, int NW, int BN>
 hipError_t launch_cfg(const AvfLaunchArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN>), dim3((uint32_t)a.num_tiles), dim3(NW * 64), 0, stream, a);
+    if (a.causal)
+        hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true>), dim3((uint32_t)a.num_tiles), dim3(NW * 64), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false>), dim3((uint32_t)a.num_tiles), dim3(NW * 64), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

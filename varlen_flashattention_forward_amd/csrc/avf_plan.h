@@ -23,6 +23,12 @@ struct AvfLaunchArgs {
     float* lse;
     // element strides (int64: offsets are formed in 64-bit arithmetic)
     int64_t q_row, q_head, k_row, k_head, v_row, v_head, o_row, o_head, lse_head;
+    // per-segment base offsets (elements) for batched [W, S, H, D] tensors:
+    // segment s (global index seg0 + local s) adds s * *_seg to its base;
+    // all zero for packed varlen tensors
+    int64_t q_seg, k_seg, v_seg, o_seg, lse_seg;
+    int32_t seg0;       // global index of this launch's first segment
+    int32_t causal;     // 1: query row r of a segment sees keys j <= r + Lk - Lq
     float scale_log2e;  // softmax_scale * log2(e): logits in base-2 units
     float scale;        // softmax_scale: the LSE is reported in natural-log units
     int32_t num_heads;

@@ -19,6 +19,9 @@ the pages' workloads are a private video model and a private training job):
   cat([attn, mlp]) layout of the "_bwd_preprocess" overflow page).
 * ``dense_117k``: S=117000, H=56, D=128, N(0,1) (the ~117k-token generation
   of the ffpa-attn page's "Verification").
+* ``causal_77k``: ``dense_77k`` with the causal mask (query row r of a segment
+  sees keys j <= r + Lk - Lq); the pages only run causal=False, so this is an
+  extension, with FLOPs counted over the visible (query, key) pairs.
 """
 from __future__ import annotations
 
@@ -39,6 +42,7 @@ class Workload:
     self_attention: bool        # cu_q == cu_k, q/k/v drawn together
     layout: str = "contiguous"  # or "stride9728"
     outer_stride: int = 0       # elements per token row of the shared buffer
+    causal: bool = False        # row r of a segment sees keys j <= r + Lk - Lq
     notes: str = field(default="", compare=False)
 
     @property
@@ -65,13 +69,28 @@ class Workload:
     def softmax_scale(self) -> float:
         return 1.0 / math.sqrt(self.head_dim)
 
+    def visible_keys(self, row: int) -> int:
+        """Keys global query row `row` attends to (all of its segment's unless causal)."""
+        b = max(i for i in range(self.num_segments) if self.cu_q[i] <= row)
+        lq = self.cu_q[b + 1] - self.cu_q[b]
+        lk = self.cu_k[b + 1] - self.cu_k[b]
+        if not self.causal:
+            return lk
+        return max(0, min(lk, row - self.cu_q[b] + lk - lq + 1))
+
     def flops(self) -> int:
-        """4 * Lq * Lk * D * H summed over segments (exact integer)."""
+        """4 * D * H * (attended (query, key) pairs) summed over segments, an
+        exact integer: 4 * Lq * Lk * D * H per segment without the causal mask."""
         tot = 0
         for b in range(self.num_segments):
             lq = self.cu_q[b + 1] - self.cu_q[b]
             lk = self.cu_k[b + 1] - self.cu_k[b]
-            tot += 4 * lq * lk * self.head_dim * self.num_heads
+            if self.causal:
+                # row r sees clamp(r + lk - lq + 1, 0, lk) keys
+                pairs = sum(max(0, min(lk, r + lk - lq + 1)) for r in range(lq))
+            else:
+                pairs = lq * lk
+            tot += 4 * pairs * self.head_dim * self.num_heads
         return tot
 
     def algorithmic_bytes(self) -> int:
@@ -94,6 +113,7 @@ WORKLOADS = {
     "strided_9728": Workload("strided_9728", 16, 96, (0, 225304, 410923), (0, 225304, 410923),
                              0.1, True, layout="stride9728", outer_stride=9728),
     "dense_117k": Workload("dense_117k", 56, 128, (0, 117000), (0, 117000), 1.0, True),
+    "causal_77k": Workload("causal_77k", 56, 128, (0, 77000), (0, 77000), 1.0, True, causal=True),
 }
 
 #: Canary written into the parts of an output buffer the kernel must not touch.
@@ -101,11 +121,11 @@ CANARY = -1234.0  # exactly representable in bf16
 
 
 def custom(name: str, num_heads: int, head_dim: int, cu_q, cu_k=None, std: float = 0.1,
-           layout: str = "contiguous", outer_stride: int = 0) -> Workload:
+           layout: str = "contiguous", outer_stride: int = 0, causal: bool = False) -> Workload:
     cu_q = tuple(int(x) for x in cu_q)
     self_attn = cu_k is None
     cu_k = cu_q if cu_k is None else tuple(int(x) for x in cu_k)
-    return Workload(name, num_heads, head_dim, cu_q, cu_k, std, self_attn, layout, outer_stride)
+    return Workload(name, num_heads, head_dim, cu_q, cu_k, std, self_attn, layout, outer_stride, causal)
 
 
 def _generator(device, seed: int) -> torch.Generator:
