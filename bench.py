@@ -26,7 +26,8 @@ sys.path.insert(0, str(ROOT))
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 KERNEL_SOURCES = ["varlen_flashattention_forward_amd/csrc/avf_kernel.hip",
-                  "varlen_flashattention_forward_amd/csrc/avf_plan.h"]
+                  "varlen_flashattention_forward_amd/csrc/avf_plan.h",
+                  "varlen_flashattention_forward_amd/csrc/avf_device.h"]
 
 
 def log(*a):

@@ -1,6 +1,7 @@
 /*
  * attn_varlen.h: C ABI of the MI355X (gfx950) packed variable-length
- * attention forward library (libattn_varlen.so).
+ * attention library (libattn_varlen.so): the forward, and its backward
+ * (section "Backward" below).
  *
  * Operation. For every segment b, with query rows [cu_q[b], cu_q[b+1]) and
  * key/value rows [cu_k[b], cu_k[b+1]), every head h and every query row i of
@@ -247,6 +248,115 @@ int32_t attn_fwd_batched_validate(const void* q, const void* k, const void* v, i
                                   int32_t head_dim, const attn_batched_layout* layout,
                                   float softmax_scale, uint32_t flags, const void* out,
                                   const float* lse);
+
+/*
+ * ---- Backward -------------------------------------------------------------
+ *
+ * Gradients of the varlen forward above for an upstream gradient
+ * dout = dL/dO: the backward of flash_attn_varlen_func on the "[FA4] cute
+ * varlen backward: int32 overflow in _bwd_preprocess ..." page ("Summary";
+ * its failing case is a dout view [410923, 16, 96] with row stride 9728 over
+ * cu_seqlens [0, 225304, 410923], "Verified sample"). With
+ * P[i,j] = exp(scale * Q[i].K[j] - LSE[i]) over the keys j row i sees (its
+ * segment's, or with ATTN_VARLEN_CAUSAL the same prefix as the forward), per
+ * head h:
+ *     D[h,i]  = sum_d out[i,h,d] * dout[i,h,d]            (preprocessing pass)
+ *     dS[i,j] = P[i,j] * (dout[i,h,:] . V[j,h,:] - D[h,i])
+ *     dQ[i]   = scale * sum_j dS[i,j] K[j],   dK[j] = scale * sum_i dS[i,j] Q[i]
+ *     dV[j]   = sum_i P[i,j] dout[i]
+ * The page names the preprocessing kernel but not its formula; D above is
+ * the library's reading of a per-row reduction over dout and out. out and
+ * lse must be the forward's outputs for the same q, k, v, scale and flags.
+ * Every gradient element is written by one wave exactly once (no atomics),
+ * so results are bitwise reproducible run to run. Rows that see no key get
+ * dQ = 0; keys no row sees get dK = dV = 0.
+ *
+ * Layout (strides in ELEMENTS, D contiguous, every offset formed in int64):
+ * q, out, dout, dq: [total_q, H, D] under their own row/head strides; k, v,
+ * dk, dv: [total_k, H, D]; lse and delta: fp32, element (h, i) at
+ * [h*lse_head + i] / [h*delta_head + i]. Row strides in [1,
+ * ATTN_VARLEN_MAX_ROW_STRIDE], head strides >= 0, all multiples of 8; bf16
+ * pointers 16-byte aligned, fp32 pointers 4-byte aligned; dq, dk and dv must
+ * not overlap themselves; lse_head and delta_head >= cu_q[B] when H > 1.
+ */
+typedef struct attn_varlen_bwd_layout {
+    int64_t q_row, q_head;
+    int64_t k_row, k_head;
+    int64_t v_row, v_head;
+    int64_t o_row, o_head;
+    int64_t do_row, do_head;
+    int64_t dq_row, dq_head;
+    int64_t dk_row, dk_head;
+    int64_t dv_row, dv_head;
+    int64_t lse_head;   /* lse[h*lse_head + i]; 0 selects q_tokens */
+    int64_t delta_head; /* delta[h*delta_head + i]; 0 selects q_tokens */
+    int64_t q_tokens;   /* rows addressable in q, out, dout, dq; cu_q[B] <= q_tokens */
+    int64_t k_tokens;   /* rows addressable in k, v, dk, dv; cu_k[B] <= k_tokens */
+} attn_varlen_bwd_layout;
+
+/*
+ * Preprocessing pass alone: delta[h*delta_head + i] = sum_d out[i,h,d] *
+ * dout[i,h,d] (fp32) for rows i in [0, rows) and every head, reading out
+ * and dout under their own strides (the page's dout view: row stride 9728).
+ * rows >= 0 (0 is a no-op); strides and alignment as in the layout above;
+ * delta_head >= rows when num_heads > 1. Enqueues one kernel on `stream`.
+ */
+int32_t attn_varlen_bwd_preprocess(const void* out, const void* dout, int64_t rows,
+                                   int32_t num_heads, int32_t head_dim, int64_t o_row,
+                                   int64_t o_head, int64_t do_row, int64_t do_head, float* delta,
+                                   int64_t delta_head, void* stream);
+
+/*
+ * Full backward with cu_seqlens in DEVICE memory (copied to the host and
+ * waited for, as in attn_varlen_fwd): the preprocessing pass into `delta`,
+ * then the dK/dV and dQ kernels, all on `stream`.
+ *   q, k, v, out, dout, lse  the forward's inputs and outputs and the
+ *                            upstream gradient (read only).
+ *   delta                    fp32 workspace [H, >= total_q] the call
+ *                            overwrites (the caller owns it; it holds D
+ *                            afterwards).
+ *   dq, dk, dv               bf16 outputs, overwritten on every row of the
+ *                            segments; rows outside them are not touched.
+ *   flags                    0 or ATTN_VARLEN_CAUSAL (as in the forward).
+ * Other arguments and errors as in attn_varlen_fwd.
+ */
+int32_t attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, int32_t num_segments, int32_t num_heads,
+                        int32_t head_dim, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                        const attn_varlen_bwd_layout* layout, float softmax_scale,
+                        uint32_t flags, float* delta, void* dq, void* dk, void* dv, void* stream);
+
+/* attn_varlen_bwd with cu_seqlens in HOST memory: no copy, no synchronisation. */
+int32_t attn_varlen_bwd_hostcu(const void* q, const void* k, const void* v, const void* out,
+                               const void* dout, const float* lse,
+                               const int32_t* cu_seqlens_q_host,
+                               const int32_t* cu_seqlens_k_host, int32_t num_segments,
+                               int32_t num_heads, int32_t head_dim, int32_t max_seqlen_q,
+                               int32_t max_seqlen_k, const attn_varlen_bwd_layout* layout,
+                               float softmax_scale, uint32_t flags, float* delta, void* dq,
+                               void* dk, void* dv, void* stream);
+
+/* Argument check of attn_varlen_bwd_hostcu without any HIP call. */
+int32_t attn_varlen_bwd_validate(const void* q, const void* k, const void* v, const void* out,
+                                 const void* dout, const float* lse,
+                                 const int32_t* cu_seqlens_q_host,
+                                 const int32_t* cu_seqlens_k_host, int32_t num_segments,
+                                 int32_t num_heads, int32_t head_dim, int32_t max_seqlen_q,
+                                 int32_t max_seqlen_k, const attn_varlen_bwd_layout* layout,
+                                 float softmax_scale, uint32_t flags, const float* delta,
+                                 const void* dq, const void* dk, const void* dv);
+
+/*
+ * Workgroups of the three backward kernels for these host cu_seqlens:
+ * preprocessing, dK/dV (tiles of keys) and dQ (tiles of query rows), and the
+ * number of dK/dV and dQ launches (segments are split as in the forward).
+ */
+int32_t attn_varlen_bwd_grid_plan(const int32_t* cu_seqlens_q_host,
+                                  const int32_t* cu_seqlens_k_host, int32_t num_segments,
+                                  int32_t num_heads, int32_t head_dim, int64_t* pre_workgroups,
+                                  int64_t* dkdv_workgroups, int64_t* dq_workgroups,
+                                  int64_t* launches);
 
 #ifdef __cplusplus
 }

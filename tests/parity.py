@@ -51,3 +51,34 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, label=""):
         stats["max_lse"] = dl
         assert dl <= LSE_ABS, f"{label}: max |dLSE| {dl:.3e} > {LSE_ABS}"
     return stats
+
+
+# Gradients (dq, dk, dv) of the backward. The _bwd_preprocess page's repro
+# accepts a gradient when max|G - G_ref| / max|G_ref| < 1e-2 (its REL_TOL,
+# "bf16 noise floor"); the per-head cosine bound is ours.
+GRAD_REL = 1e-2
+GRAD_COS = 0.9999
+
+
+def compare_grad(g_gpu, g_ref, label=""):
+    """g_*: [R, H, D] numpy. Relative max error against the reference's max
+    magnitude, per-head cosine, finiteness. Returns stats; raises on failure."""
+    g_gpu = np.asarray(g_gpu, dtype=np.float64)
+    g_ref = np.asarray(g_ref, dtype=np.float64)
+    assert g_gpu.shape == g_ref.shape, (g_gpu.shape, g_ref.shape)
+    assert np.all(np.isfinite(g_gpu)), f"{label}: non-finite gradient"
+    scale = float(np.abs(g_ref).max()) if g_ref.size else 0.0
+    err = float(np.abs(g_gpu - g_ref).max()) if g_ref.size else 0.0
+    if scale == 0.0:
+        assert err == 0.0, f"{label}: reference is zero but the gradient is not ({err:.3e})"
+        return {"rel": 0.0, "min_cos": 1.0}
+    rel = err / scale
+    cos = []
+    for h in range(g_ref.shape[1]):
+        a, b = g_gpu[:, h].ravel(), g_ref[:, h].ravel()
+        na, nb = np.linalg.norm(a), np.linalg.norm(b)
+        cos.append(1.0 if na == 0 and nb == 0 else (0.0 if na == 0 or nb == 0 else float(a @ b / (na * nb))))
+    stats = {"rel": rel, "min_cos": min(cos)}
+    assert rel < GRAD_REL, f"{label}: max|dG|/max|G| {rel:.3e} >= {GRAD_REL}"
+    assert min(cos) >= GRAD_COS, f"{label}: min per-head cosine {min(cos):.6f} < {GRAD_COS}"
+    return stats

@@ -1,0 +1,222 @@
+"""GPU tests of the backward (preprocessing pass, dK/dV and dQ kernels)
+against the CPU oracle's exact fp64 gradients, through the C ABI. Marked
+`gpu`; every case prints its name before it touches the GPU.
+
+The forward's out and lse fed to the backward come from the library's own
+forward (its parity is tested separately); the oracle's gradients depend on
+q, k, v and dout only.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import varlen_flashattention_forward_amd as avf
+from varlen_flashattention_forward_amd.workloads import WORKLOADS, custom, make_dout, make_inputs, sample_rows
+
+from parity import compare_grad
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(label):
+    print(f"\n[gpu-case] {label}", flush=True)
+
+
+def f32(x):
+    return float(np.float32(x))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    avf.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def forward(t, w, causal):
+    o, l = avf.attn_varlen_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                               softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"], causal=causal,
+                               cu_seqlens_q_host=list(w.cu_q), cu_seqlens_k_host=list(w.cu_k))
+    return o, l
+
+
+def backward(t, w, dout, causal, hostcu=True, **kw):
+    o, l = forward(t, w, causal)
+    cu = dict(cu_seqlens_q_host=list(w.cu_q), cu_seqlens_k_host=list(w.cu_k)) if hostcu else {}
+    r = avf.attn_varlen_bwd(t["q"], t["k"], t["v"], o, dout, l, t["cu_q"], t["cu_k"], w.max_seqlen_q,
+                            w.max_seqlen_k, softmax_scale=w.softmax_scale, causal=causal, **cu, **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def oracle_grads(t, w, dout, causal):
+    q, k, v = (t[n].contiguous().cpu() for n in ("q", "k", "v"))
+    return oracle.attn_varlen_bwd(q, k, v, dout.contiguous().cpu(), w.cu_q, w.cu_k, f32(w.softmax_scale),
+                                  causal=causal)
+
+
+def check_all(label, got, ref, w):
+    """Compare dq over the segments' query rows and dk/dv over their key rows."""
+    dq, dk, dv = (x.float().cpu().numpy() for x in got[:3])
+    rq, rk, rv = ref
+    nq, nk = w.total_q, w.total_k
+    stats = {}
+    for name, g, r, n in (("dq", dq, rq, nq), ("dk", dk, rk, nk), ("dv", dv, rv, nk)):
+        if n:
+            stats[name] = compare_grad(g[:n], r[:n], f"{label} {name}")
+    print(f"[{label}] {stats}", flush=True)
+    return stats
+
+
+# ------------------------------------------------------------------ small full-oracle cases
+
+SMALL = {
+    # several dK/dV and dQ tiles, ragged tails, Lq != Lk, one-row and one-key segments
+    "ragged_d128": (128, 2, [0, 1, 300, 300, 813, 1100], [0, 70, 71, 104, 744, 873]),
+    "ragged_d96": (96, 3, [0, 129, 190, 577], [0, 64, 321, 322]),
+    "ragged_d64": (64, 2, [0, 255, 256, 700], [0, 300, 301, 450]),
+    "self_d128": (128, 1, [0, 640, 1000], None),
+}
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_bwd_small_full_oracle(name, causal):
+    D, H, cu_q, cu_k = SMALL[name]
+    announce(f"bwd {name} causal={causal}")
+    w = custom(name, H, D, cu_q, cu_k, std=1.0)
+    t = make_inputs(w, "cuda", seed=3)
+    dout, _ = make_dout(w, "cuda", seed=4)
+    got = backward(t, w, dout, causal)
+    check_all(f"{name} causal={causal}", got, oracle_grads(t, w, dout, causal), w)
+
+
+def test_bwd_empty_segments():
+    """Lk = 0 segment: dq = 0; Lq = 0 segment: its keys get dk = dv = 0."""
+    announce("bwd empty segments")
+    w = custom("empty", 2, 64, [0, 40, 40, 90], [0, 0, 33, 70], std=1.0)
+    t = make_inputs(w, "cuda", seed=5)
+    dout, _ = make_dout(w, "cuda", seed=6)
+    dq, dk, dv, _ = backward(t, w, dout, False)
+    assert torch.count_nonzero(dq[0:40]).item() == 0
+    assert torch.count_nonzero(dk[0:33]).item() == 0 and torch.count_nonzero(dv[0:33]).item() == 0
+    check_all("empty", (dq, dk, dv), oracle_grads(t, w, dout, False), w)
+
+
+def test_bwd_causal_rows_without_keys():
+    """Lq > Lk causal: rows r < Lq - Lk see no key and get dq = 0."""
+    announce("bwd causal rows without keys")
+    w = custom("nokeys", 2, 128, [0, 300], [0, 100], std=1.0)
+    t = make_inputs(w, "cuda", seed=7)
+    dout, _ = make_dout(w, "cuda", seed=8)
+    dq, dk, dv, _ = backward(t, w, dout, True)
+    assert torch.count_nonzero(dq[0:200]).item() == 0
+    check_all("nokeys", (dq, dk, dv), oracle_grads(t, w, dout, True), w)
+
+
+def test_bwd_deterministic_hostcu_and_device_cu():
+    announce("bwd determinism / device cu")
+    w = custom("det", 2, 96, [0, 500, 777], [0, 260, 777], std=1.0)
+    t = make_inputs(w, "cuda", seed=9)
+    dout, _ = make_dout(w, "cuda", seed=10)
+    a = backward(t, w, dout, False)
+    b = backward(t, w, dout, False)
+    c = backward(t, w, dout, False, hostcu=False)
+    for x, y, z in zip(a[:3], b[:3], c[:3]):
+        assert torch.equal(x, y) and torch.equal(x, z)
+
+
+def test_bwd_strided_dout_equals_contiguous_small():
+    """The page's test at small size: dout as a row-stride-9728 view vs its
+    contiguous copy gives bitwise identical gradients; both match the oracle."""
+    announce("bwd strided dout small")
+    w = custom("strided_small", 16, 96, [0, 700, 1300], std=0.1)
+    t = make_inputs(w, "cuda", seed=11)
+    dout, base = make_dout(w, "cuda", seed=12, outer_stride=9728)
+    assert dout.stride() == (9728, 96, 1)
+    a = backward(t, w, dout, False)
+    b = backward(t, w, dout.contiguous(), False)
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x, y)
+    check_all("strided_small", a, oracle_grads(t, w, dout, False), w)
+
+
+def test_bwd_preprocess_matches_oracle_strided():
+    announce("bwd preprocess strided")
+    w = custom("pre", 16, 96, [0, 3000], std=0.1)
+    o, _ = make_dout(w, "cuda", seed=13, outer_stride=9728)
+    g, _ = make_dout(w, "cuda", seed=14, outer_stride=9728)
+    delta = avf.bwd_preprocess(o, g)
+    torch.cuda.synchronize()
+    ref = oracle.bwd_preprocess(o.contiguous().cpu(), g.contiguous().cpu())  # [N, H]
+    got = delta.t().cpu().numpy().astype(np.float64)
+    assert np.abs(got - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("D", [64, 96, 128])
+def test_bwd_output_strides(D):
+    """dq/dk/dv written into strided views of larger buffers: values equal the
+    contiguous outputs and nothing outside the views changes."""
+    announce(f"bwd output strides D={D}")
+    w = custom(f"ostr{D}", 3, D, [0, 150, 420], [0, 200, 333], std=1.0)
+    t = make_inputs(w, "cuda", seed=15)
+    dout, _ = make_dout(w, "cuda", seed=16)
+    a = backward(t, w, dout, False)
+    H = w.num_heads
+    bufs = [torch.full((n, 2 * H * D + 64), -7.0, dtype=torch.bfloat16, device="cuda") for n in (w.total_q, w.total_k, w.total_k)]
+    views = [b[:, 64:64 + 2 * H * D].view(b.shape[0], H, 2 * D)[:, :, :D] for b in bufs]
+    o, l = forward(t, w, False)
+    avf.attn_varlen_bwd(t["q"], t["k"], t["v"], o, dout, l, t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                        softmax_scale=w.softmax_scale, dq=views[0], dk=views[1], dv=views[2],
+                        cu_seqlens_q_host=list(w.cu_q), cu_seqlens_k_host=list(w.cu_k))
+    torch.cuda.synchronize()
+    for x, v_, b in zip(a[:3], views, bufs):
+        assert torch.equal(x, v_)
+        mask = torch.ones_like(b, dtype=torch.bool)
+        mask[:, 64:64 + 2 * H * D].view(b.shape[0], H, 2 * D)[:, :, :D] = False
+        assert bool((b[mask] == -7.0).all())
+
+
+# ------------------------------------------------------------------ the page's full-size case
+
+def test_bwd_full_size_strided_dout():
+    """N=410923, H=16, D=96, cu=[0,225304,410923], dout row stride 9728 (the
+    _bwd_preprocess page's failing case, 225304 * 9728 > 2^31): gradients
+    bitwise equal to those of a contiguous dout, dq on sampled rows against the
+    oracle, and the invariants sum_j dk_j = 0 and sum_j dv_j = sum_i dout_i
+    per segment and head (they hold at any size)."""
+    w = WORKLOADS["bwd_9728"]
+    announce("bwd full size bwd_9728")
+    t = make_inputs(w, "cuda", seed=0)
+    dout, base = make_dout(w, "cuda", seed=1, outer_stride=9728)
+    assert 225304 * dout.stride(0) > 2 ** 31
+    a = backward(t, w, dout, False)
+    b = backward(t, w, dout.contiguous(), False)
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x, y)
+    del b
+    dq, dk, dv, _ = a
+    rows = sample_rows(w, 16, edge=4)
+    q, k, v = (t[n].contiguous().cpu() for n in ("q", "k", "v"))
+    ref = oracle.attn_varlen_bwd_dq_rows(q, k, v, dout.contiguous().cpu(), w.cu_q, w.cu_k, f32(w.softmax_scale),
+                                         rows)
+    compare_grad(dq[rows].float().cpu().numpy(), ref, "bwd_9728 dq rows")
+    g64 = dout.double()
+    for s in range(w.num_segments):
+        ks = slice(w.cu_k[s], w.cu_k[s + 1])
+        qs = slice(w.cu_q[s], w.cu_q[s + 1])
+        sdk = dk[ks].double().sum(0)          # [H, D], exactly 0 in exact arithmetic
+        sdv = dv[ks].double().sum(0)
+        sg = g64[qs].sum(0)
+        # dv: rounding P to bf16 moves each row's weight sum by at most 2^-9
+        # and rounding dv by 2^-9 of |dv|; twice that bound. dk: twice the
+        # output rounding (the weight-sum terms cancel up to random rounding).
+        tol_k = 2.0 ** -8 * dk[ks].double().abs().sum(0) + 1e-6
+        tol_v = 2.0 ** -8 * (dv[ks].double().abs().sum(0) + g64[qs].abs().sum(0)) + 1e-6
+        print(f"[bwd_9728] segment {s}: max|sum dk| {sdk.abs().max().item():.3e} "
+              f"max|sum dv - sum dout| {(sdv - sg).abs().max().item():.3e}", flush=True)
+        assert bool((sdk.abs() <= tol_k).all()), s
+        assert bool(((sdv - sg).abs() <= tol_v).all()), s

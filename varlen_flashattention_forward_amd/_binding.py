@@ -26,6 +26,8 @@ EXPORTED_SYMBOLS = (
     "attn_varlen_decode_tile", "attn_varlen_element_offset", "attn_varlen_last_error",
     "attn_varlen_fwd_ex", "attn_varlen_fwd_hostcu_ex", "attn_varlen_validate_ex",
     "attn_fwd_batched", "attn_fwd_batched_validate",
+    "attn_varlen_bwd_preprocess", "attn_varlen_bwd", "attn_varlen_bwd_hostcu", "attn_varlen_bwd_validate",
+    "attn_varlen_bwd_grid_plan",
 )
 
 CAUSAL = 1  # ATTN_VARLEN_CAUSAL
@@ -47,6 +49,13 @@ class BatchedLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "q_batch", "q_row", "q_head", "k_batch", "k_row", "k_head", "v_batch", "v_row", "v_head",
         "o_batch", "o_row", "o_head", "lse_batch", "lse_head")]
+
+
+class BwdLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "q_row", "q_head", "k_row", "k_head", "v_row", "v_head", "o_row", "o_head", "do_row", "do_head",
+        "dq_row", "dq_head", "dk_row", "dk_head", "dv_row", "dv_head", "lse_head", "delta_head",
+        "q_tokens", "k_tokens")]
 
 
 _lib = None
@@ -85,6 +94,20 @@ def lib():
         L.attn_fwd_batched.argtypes = b_args
         L.attn_fwd_batched_validate.restype = ctypes.c_int32
         L.attn_fwd_batched_validate.argtypes = b_args[:-1]
+        L.attn_varlen_bwd_preprocess.restype = ctypes.c_int32
+        L.attn_varlen_bwd_preprocess.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] + \
+            [ctypes.c_int64] * 4 + [_vp, ctypes.c_int64, _vp]
+        bwd_args = [_vp] * 8 + [ctypes.c_int32] * 5 + [ctypes.POINTER(BwdLayout), ctypes.c_float, ctypes.c_uint32,
+                                                      _vp, _vp, _vp, _vp, _vp]
+        for name in ("attn_varlen_bwd", "attn_varlen_bwd_hostcu"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int32
+            f.argtypes = bwd_args
+        L.attn_varlen_bwd_validate.restype = ctypes.c_int32
+        L.attn_varlen_bwd_validate.argtypes = bwd_args[:-1]
+        L.attn_varlen_bwd_grid_plan.restype = ctypes.c_int32
+        L.attn_varlen_bwd_grid_plan.argtypes = [_i32p, _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                _i64p, _i64p, _i64p, _i64p]
         L.attn_varlen_block_m.restype = ctypes.c_int32
         L.attn_varlen_block_m.argtypes = [ctypes.c_int32]
         L.attn_varlen_count_tiles.restype = ctypes.c_int64
@@ -296,3 +319,118 @@ def attn_fwd(q, k, v, softmax_scale: float | None = None, causal: bool = False, 
                                 lse.data_ptr() if lse is not None else None, stream)
     _check(rc)
     return out, lse
+
+
+# ---- backward -----------------------------------------------------------------------
+
+def bwd_grid_plan(cu_q, cu_k, num_heads: int, head_dim: int):
+    """(preprocessing, dK/dV, dQ workgroups, dK/dV + dQ launches) for host cu arrays."""
+    cq, B = _cu_array(cu_q)
+    ck, Bk = _cu_array(cu_k)
+    if Bk != B:
+        raise ValueError("cu_q and cu_k differ in length")
+    out = [ctypes.c_int64() for _ in range(4)]
+    _check(lib().attn_varlen_bwd_grid_plan(cq, ck, B, num_heads, head_dim, *(ctypes.byref(x) for x in out)))
+    return tuple(x.value for x in out)
+
+
+def validate_bwd(ptrs, cu_q, cu_k, num_heads, head_dim, max_q, max_k, layout: BwdLayout, scale: float,
+                 flags: int = 0) -> int:
+    """Return code of the backward's host-side argument check (no HIP call).
+    ptrs: (q, k, v, out, dout, lse, delta, dq, dk, dv) addresses or None."""
+    q, k, v, o, g, lse, delta, dq, dk, dv = ptrs
+    cq, B = _cu_array(cu_q)
+    ck, Bk = _cu_array(cu_k)
+    if Bk != B:
+        raise ValueError("cu_q and cu_k differ in length")
+    return lib().attn_varlen_bwd_validate(q, k, v, o, g, lse, cq, ck, B, num_heads, head_dim, max_q, max_k,
+                                          ctypes.byref(layout), scale, flags, delta, dq, dk, dv)
+
+
+def _fp32_rows(t, name, H, total_q):
+    import torch
+
+    if t.dtype != torch.float32 or t.dim() != 2 or t.shape[0] != H or t.stride(1) != 1 or t.shape[1] < total_q:
+        raise ValueError(f"{name} must be fp32 [H, >= total_q] with unit inner stride")
+    return t.stride(0)
+
+
+def bwd_preprocess(out, dout, delta=None, stream=None):
+    """D[h, i] = sum_d out[i,h,d] * dout[i,h,d] (fp32 [H, total_q]) for bf16
+    [total_q, H, D] device tensors with any row/head strides."""
+    import torch
+
+    if out.dtype != torch.bfloat16 or dout.dtype != torch.bfloat16 or out.shape != dout.shape or out.dim() != 3:
+        raise ValueError("out and dout must be bf16 [total_q, H, D] of one shape")
+    if out.stride(2) != 1 or dout.stride(2) != 1:
+        raise ValueError("out and dout must have a contiguous D dimension")
+    total_q, H, D = out.shape
+    if delta is None:
+        delta = torch.empty((H, total_q), dtype=torch.float32, device=out.device)
+    dh = _fp32_rows(delta, "delta", H, total_q)
+    if stream is None:
+        stream = torch.cuda.current_stream(out.device).cuda_stream
+    _check(lib().attn_varlen_bwd_preprocess(out.data_ptr(), dout.data_ptr(), total_q, H, D, out.stride(0),
+                                            out.stride(1), dout.stride(0), dout.stride(1), delta.data_ptr(), dh,
+                                            stream))
+    return delta
+
+
+def attn_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    softmax_scale: float | None = None, causal: bool = False, dq=None, dk=None, dv=None,
+                    delta=None, cu_seqlens_q_host=None, cu_seqlens_k_host=None, stream=None):
+    """Varlen attention backward on torch's current stream.
+
+    q, out, dout: [total_q, H, D]; k, v: [total_k, H, D] bf16 device tensors
+    (any token and head strides, contiguous D); lse: the forward's fp32
+    [H, >= total_q]. dq/dk/dv (bf16, q's / k's shape) and the fp32 workspace
+    delta [H, >= total_q] are allocated when not given. With host copies of
+    cu_seqlens the synchronisation-free entry point is used.
+    Returns (dq, dk, dv, delta).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{name} must be a bf16 device tensor [tokens, H, D] with contiguous D")
+    total_q, H, D = q.shape
+    if k.shape[1:] != (H, D) or v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("k, v must be [total_k, H, D]; out and dout q's shape")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.dtype != torch.bfloat16 or t.shape != ref.shape or t.stride(2) != 1:
+            raise ValueError(f"{name} must be bf16 with {('q', 'k', 'v')[('dq', 'dk', 'dv').index(name)]}'s shape")
+    if delta is None:
+        delta = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    lh = _fp32_rows(lse, "lse", H, total_q)
+    dh = _fp32_rows(delta, "delta", H, total_q)
+    layout = BwdLayout(q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+                       out.stride(0), out.stride(1), dout.stride(0), dout.stride(1), dq.stride(0), dq.stride(1),
+                       dk.stride(0), dk.stride(1), dv.stride(0), dv.stride(1), lh, dh, total_q, k.shape[0])
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr())
+    tail = (ctypes.byref(layout), float(softmax_scale), CAUSAL if causal else 0, delta.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), stream)
+    L = lib()
+    if cu_seqlens_q_host is not None or cu_seqlens_k_host is not None:
+        cq, B = _cu_array(cu_seqlens_q_host)
+        ck, Bk = _cu_array(cu_seqlens_k_host)
+        if B != Bk:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+        rc = L.attn_varlen_bwd_hostcu(*ptrs, cq, ck, B, H, D, int(max_seqlen_q), int(max_seqlen_k), *tail)
+    else:
+        for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+            if cu.dtype != torch.int32 or not cu.is_cuda or cu.dim() != 1 or not cu.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous int32 device tensor")
+        B = cu_seqlens_q.numel() - 1
+        if cu_seqlens_k.numel() != B + 1:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+        rc = L.attn_varlen_bwd(*ptrs, cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, D,
+                               int(max_seqlen_q), int(max_seqlen_k), *tail)
+    _check(rc)
+    return dq, dk, dv, delta

@@ -20,7 +20,7 @@ CSRC = PKG / "csrc"
 ROOT = PKG.parent
 LIB = Path(os.environ.get("AVF_LIB_OUT", PKG / "libattn_varlen.so"))
 BUILD_DIR = Path(os.environ.get("AVF_BUILD_DIR", PKG / "_build"))
-SOURCES = ["avf_api.hip", "avf_kernel.hip"]
+SOURCES = ["avf_api.hip", "avf_kernel.hip", "avf_bwd_kernel.hip"]
 ARCH = os.environ.get("AVF_OFFLOAD_ARCH", "gfx950")
 
 
@@ -31,13 +31,17 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libattn_varlen.so)")
 
 
-def common_flags() -> list:
-    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
-            f"-I{ROOT / 'include'}", f"-I{CSRC}",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # MFMA accumulators in architectural VGPRs, so the softmax rescale
-            # and epilogue touch them without AGPR<->VGPR copies
-            "-mllvm", "-amdgpu-mfma-vgpr-form=1"] + extra_flags()
+def common_flags(src: str = "avf_kernel.hip") -> list:
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+             f"-I{ROOT / 'include'}", f"-I{CSRC}",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    if src != "avf_bwd_kernel.hip":
+        # forward: MFMA accumulators in architectural VGPRs, so the softmax
+        # rescale and epilogue touch them without AGPR<->VGPR copies. The
+        # backward kernels keep more accumulators than 256 VGPRs hold and
+        # leave the choice to the compiler.
+        flags += ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+    return flags + extra_flags()
 
 
 def extra_flags() -> list:
@@ -47,7 +51,7 @@ def extra_flags() -> list:
 
 def _compile(src: str) -> Path:
     obj = BUILD_DIR / (Path(src).stem + ".o")
-    cmd = [hipcc(), "-c", str(CSRC / src), "-o", str(obj)] + common_flags()
+    cmd = [hipcc(), "-c", str(CSRC / src), "-o", str(obj)] + common_flags(src)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

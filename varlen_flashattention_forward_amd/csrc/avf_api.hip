@@ -1,5 +1,5 @@
-// C ABI of the packed variable-length attention forward: argument checks,
-// the exact tile plan, and the launches. Declarations and contracts are in
+// C ABI of the packed variable-length attention forward and backward:
+// argument checks, the exact tile plans, and the launches. Declarations and contracts are in
 // include/attn_varlen.h.
 
 #include <hip/hip_runtime.h>
@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "../../include/attn_varlen.h"
+#include "avf_bwd_plan.h"
 #include "avf_plan.h"
 
 namespace {
@@ -451,5 +452,284 @@ int64_t attn_varlen_element_offset(int64_t row, int64_t row_stride, int64_t head
 }
 
 const char* attn_varlen_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward
+
+namespace {
+
+// Token-row / head strides of one bf16 [rows, H, D] tensor.
+int32_t check_strides(const char* name, int64_t row, int64_t head) {
+    if (row < 1 || head < 0)
+        return fail(ATTN_VARLEN_EINVAL, "%s strides must be row >= 1, head >= 0 (got %lld, %lld)", name,
+                    (long long)row, (long long)head);
+    if ((row & 7) || (head & 7))
+        return fail(ATTN_VARLEN_EALIGN, "%s strides must be multiples of 8 elements (got %lld, %lld)", name,
+                    (long long)row, (long long)head);
+    if (row > ATTN_VARLEN_MAX_ROW_STRIDE)
+        return fail(ATTN_VARLEN_EUNSUPPORTED, "%s row stride %lld exceeds the limit %lld", name, (long long)row,
+                    (long long)ATTN_VARLEN_MAX_ROW_STRIDE);
+    return ATTN_VARLEN_OK;
+}
+
+int32_t check_fp32_head(const char* name, int64_t head, int64_t rows, int32_t H) {
+    if (head < 0) return fail(ATTN_VARLEN_EINVAL, "%s_head must be >= 0", name);
+    if (H > 1 && head < rows)
+        return fail(ATTN_VARLEN_EINVAL, "%s_head %lld is smaller than the %lld rows", name, (long long)head,
+                    (long long)rows);
+    return ATTN_VARLEN_OK;
+}
+
+int32_t bwd_check_scalars(const void* q, const void* k, const void* v, const void* o, const void* g,
+                          const float* lse, int32_t B, int32_t H, int32_t D, int32_t max_q, int32_t max_k,
+                          const attn_varlen_bwd_layout* st, float scale, uint32_t flags, const float* delta,
+                          const void* dq, const void* dk, const void* dv) {
+    int32_t rc = check_flags(flags);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    if (B < 0) return fail(ATTN_VARLEN_EINVAL, "num_segments must be >= 0 (got %d)", B);
+    if (H <= 0) return fail(ATTN_VARLEN_EINVAL, "num_heads must be >= 1 (got %d)", H);
+    if (max_q < 0 || max_k < 0)
+        return fail(ATTN_VARLEN_EINVAL, "max_seqlen_q/k must be >= 0 (got %d, %d)", max_q, max_k);
+    if (!st) return fail(ATTN_VARLEN_ENULL, "layout is NULL");
+    if (st->q_tokens < 0 || st->k_tokens < 0 || st->q_tokens > INT32_MAX || st->k_tokens > INT32_MAX)
+        return fail(ATTN_VARLEN_EINVAL, "q_tokens/k_tokens must be in [0, 2^31) (got %lld, %lld)",
+                    (long long)st->q_tokens, (long long)st->k_tokens);
+    if (avf_bwd_block_n(D) <= 0)
+        return fail(ATTN_VARLEN_EUNSUPPORTED, "head_dim %d not supported (64, 96 or 128)", D);
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(ATTN_VARLEN_EINVAL, "softmax_scale must be finite and > 0 (got %g)", (double)scale);
+    if (B == 0) return ATTN_VARLEN_OK;
+    if (st->q_tokens > 0 && (!q || !o || !g || !dq || !lse || !delta))
+        return fail(ATTN_VARLEN_ENULL, "q, out, dout, dq, lse and delta must be non-NULL");
+    if (st->k_tokens > 0 && (!k || !v || !dk || !dv))
+        return fail(ATTN_VARLEN_ENULL, "k, v, dk and dv must be non-NULL");
+    const void* bf[8] = {q, k, v, o, g, dq, dk, dv};
+    for (const void* p : bf)
+        if (!aligned16(p)) return fail(ATTN_VARLEN_EALIGN, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(delta) & 3u))
+        return fail(ATTN_VARLEN_EALIGN, "lse and delta must be 4-byte aligned");
+    const struct { const char* n; int64_t r, h; } t[8] = {
+        {"q", st->q_row, st->q_head},    {"k", st->k_row, st->k_head},    {"v", st->v_row, st->v_head},
+        {"out", st->o_row, st->o_head},  {"dout", st->do_row, st->do_head}, {"dq", st->dq_row, st->dq_head},
+        {"dk", st->dk_row, st->dk_head}, {"dv", st->dv_row, st->dv_head}};
+    for (const auto& x : t)
+        if ((rc = check_strides(x.n, x.r, x.h)) != ATTN_VARLEN_OK) return rc;
+    return ATTN_VARLEN_OK;
+}
+
+// Checks that need the cu values (host arrays).
+int32_t bwd_check_cu(const int32_t* cu_q, const int32_t* cu_k, int32_t B, int32_t H, int32_t D, int32_t max_q,
+                     int32_t max_k, const attn_varlen_bwd_layout* st) {
+    attn_varlen_layout ext;
+    std::memset(&ext, 0, sizeof ext);
+    ext.q_tokens = st->q_tokens;
+    ext.k_tokens = st->k_tokens;
+    int32_t rc = check_cu(cu_q, cu_k, B, max_q, max_k, &ext);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    const int64_t tq = cu_q[B], tk = cu_k[B];
+    if (!non_overlapping(tq, st->dq_row, H, st->dq_head, D))
+        return fail(ATTN_VARLEN_EINVAL, "dq strides make elements overlap");
+    if (!non_overlapping(tk, st->dk_row, H, st->dk_head, D))
+        return fail(ATTN_VARLEN_EINVAL, "dk strides make elements overlap");
+    if (!non_overlapping(tk, st->dv_row, H, st->dv_head, D))
+        return fail(ATTN_VARLEN_EINVAL, "dv strides make elements overlap");
+    if ((rc = check_fp32_head("lse", st->lse_head ? st->lse_head : st->q_tokens, tq, H)) != ATTN_VARLEN_OK)
+        return rc;
+    return check_fp32_head("delta", st->delta_head ? st->delta_head : st->q_tokens, tq, H);
+}
+
+// Rows of the preprocessing pass per launch: H * rows items, 16 per
+// 256-thread workgroup, keep the grid below 2^32 work-items.
+constexpr int64_t kPreItemsPerLaunch = (int64_t)1 << 27;
+
+hipError_t preprocess(const void* o, const void* g, int64_t rows, int32_t H, int32_t D, int64_t o_row,
+                      int64_t o_head, int64_t do_row, int64_t do_head, float* delta, int64_t delta_head,
+                      hipStream_t s) {
+    const int64_t chunk = std::max<int64_t>(1, kPreItemsPerLaunch / H);
+    for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
+        AvfPreArgs p;
+        p.o = (const char*)o + 2 * r0 * o_row;
+        p.dout = (const char*)g + 2 * r0 * do_row;
+        p.delta = delta + r0;
+        p.o_row = o_row; p.o_head = o_head; p.do_row = do_row; p.do_head = do_head;
+        p.delta_head = delta_head;
+        p.rows = std::min(chunk, rows - r0);
+        p.num_heads = H;
+        const hipError_t e = avf_bwd_preprocess_launch(p, D, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// Launches of one tile kernel over all segments; `tiled` is the cu array
+// whose segment lengths are cut into blocks of `bm` (keys for dK/dV, query
+// rows for dQ). Each launch carries at most AVF_SEGS_PER_LAUNCH segments and
+// kMaxTilesPerLaunch tiles. With `count` set only counts, launching nothing.
+template <typename Launch>
+int32_t for_each_launch(AvfBwdArgs& a, const int32_t* cu_q, const int32_t* cu_k, const int32_t* tiled, int32_t B,
+                        int32_t H, int32_t bm, Launch&& launch, int64_t* launches, int64_t* workgroups) {
+    for (int32_t b0 = 0; b0 < B;) {
+        int32_t b1 = b0;
+        int64_t t = 0;
+        while (b1 < B && b1 - b0 < AVF_SEGS_PER_LAUNCH) {
+            const int64_t tb = tiles_of(tiled, b1, b1 + 1, H, bm);
+            if (t + tb > kMaxTilesPerLaunch && b1 > b0) break;
+            if (tb > kMaxTilesPerLaunch)
+                return fail(ATTN_VARLEN_EUNSUPPORTED, "segment %d needs %lld tiles (limit %lld per launch)", b1,
+                            (long long)tb, (long long)kMaxTilesPerLaunch);
+            t += tb;
+            ++b1;
+        }
+        int64_t acc = 0;
+        a.num_segs = b1 - b0;
+        for (int32_t s = 0; s <= b1 - b0; ++s) {
+            a.tile_start[s] = (int32_t)acc;
+            a.q_start[s] = cu_q[b0 + s];
+            a.k_start[s] = cu_k[b0 + s];
+            if (s < b1 - b0) acc += tiles_of(tiled, b0 + s, b0 + s + 1, H, bm);
+        }
+        a.num_tiles = (int32_t)acc;
+        if (acc > 0) {
+            if (launches) ++*launches;
+            if (workgroups) *workgroups += acc;
+            const hipError_t e = launch(a);
+            if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+        }
+        b0 = b1;
+    }
+    return ATTN_VARLEN_OK;
+}
+
+AvfBwdArgs bwd_args(const void* q, const void* k, const void* v, const void* g, const float* lse, const float* delta,
+                    void* dq, void* dk, void* dv, int32_t H, const attn_varlen_bwd_layout* st, float scale,
+                    uint32_t flags) {
+    AvfBwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q; a.k = k; a.v = v; a.dout = g; a.lse = lse; a.delta = delta; a.dq = dq; a.dk = dk; a.dv = dv;
+    a.q_row = st->q_row; a.q_head = st->q_head; a.k_row = st->k_row; a.k_head = st->k_head;
+    a.v_row = st->v_row; a.v_head = st->v_head; a.do_row = st->do_row; a.do_head = st->do_head;
+    a.dq_row = st->dq_row; a.dq_head = st->dq_head; a.dk_row = st->dk_row; a.dk_head = st->dk_head;
+    a.dv_row = st->dv_row; a.dv_head = st->dv_head;
+    a.lse_head = st->lse_head ? st->lse_head : st->q_tokens;
+    a.delta_head = st->delta_head ? st->delta_head : st->q_tokens;
+    a.scale = scale;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    a.causal = (flags & ATTN_VARLEN_CAUSAL) ? 1 : 0;
+    a.num_heads = H;
+    return a;
+}
+
+int32_t bwd_run(const void* q, const void* k, const void* v, const void* o, const void* g, const float* lse,
+                const int32_t* cu_q, const int32_t* cu_k, int32_t B, int32_t H, int32_t D,
+                const attn_varlen_bwd_layout* st, float scale, uint32_t flags, float* delta, void* dq, void* dk,
+                void* dv, hipStream_t s) {
+    const int64_t delta_head = st->delta_head ? st->delta_head : st->q_tokens;
+    hipError_t e = preprocess(o, g, cu_q[B], H, D, st->o_row, st->o_head, st->do_row, st->do_head, delta,
+                              delta_head, s);
+    if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "preprocessing launch failed: %s", hipGetErrorString(e));
+    AvfBwdArgs a = bwd_args(q, k, v, g, lse, delta, dq, dk, dv, H, st, scale, flags);
+    int32_t rc = for_each_launch(a, cu_q, cu_k, cu_k, B, H, avf_bwd_block_n(D),
+                                 [&](const AvfBwdArgs& x) { return avf_bwd_dkdv_launch(x, D, s); }, nullptr, nullptr);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    return for_each_launch(a, cu_q, cu_k, cu_q, B, H, avf_bwd_block_m(D),
+                           [&](const AvfBwdArgs& x) { return avf_bwd_dq_launch(x, D, s); }, nullptr, nullptr);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t attn_varlen_bwd_preprocess(const void* out, const void* dout, int64_t rows, int32_t H, int32_t D,
+                                   int64_t o_row, int64_t o_head, int64_t do_row, int64_t do_head, float* delta,
+                                   int64_t delta_head, void* stream) {
+    g_last_error.clear();
+    if (rows < 0 || rows > INT32_MAX) return fail(ATTN_VARLEN_EINVAL, "rows must be in [0, 2^31) (got %lld)", (long long)rows);
+    if (H <= 0) return fail(ATTN_VARLEN_EINVAL, "num_heads must be >= 1 (got %d)", H);
+    if (avf_bwd_block_n(D) <= 0)
+        return fail(ATTN_VARLEN_EUNSUPPORTED, "head_dim %d not supported (64, 96 or 128)", D);
+    if (rows == 0) return ATTN_VARLEN_OK;
+    if (!out || !dout || !delta) return fail(ATTN_VARLEN_ENULL, "out, dout and delta must be non-NULL");
+    if (!aligned16(out) || !aligned16(dout)) return fail(ATTN_VARLEN_EALIGN, "out and dout must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(delta) & 3u) return fail(ATTN_VARLEN_EALIGN, "delta must be 4-byte aligned");
+    int32_t rc = check_strides("out", o_row, o_head);
+    if (rc == ATTN_VARLEN_OK) rc = check_strides("dout", do_row, do_head);
+    if (rc == ATTN_VARLEN_OK) rc = check_fp32_head("delta", delta_head, rows, H);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    const hipError_t e = preprocess(out, dout, rows, H, D, o_row, o_head, do_row, do_head, delta, delta_head,
+                                    static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "preprocessing launch failed: %s", hipGetErrorString(e));
+    return ATTN_VARLEN_OK;
+}
+
+int32_t attn_varlen_bwd_validate(const void* q, const void* k, const void* v, const void* o, const void* g,
+                                 const float* lse, const int32_t* cu_q, const int32_t* cu_k, int32_t B, int32_t H,
+                                 int32_t D, int32_t max_q, int32_t max_k, const attn_varlen_bwd_layout* st,
+                                 float scale, uint32_t flags, const float* delta, const void* dq, const void* dk,
+                                 const void* dv) {
+    g_last_error.clear();
+    int32_t rc = bwd_check_scalars(q, k, v, o, g, lse, B, H, D, max_q, max_k, st, scale, flags, delta, dq, dk, dv);
+    if (rc != ATTN_VARLEN_OK || B == 0) return rc;
+    return bwd_check_cu(cu_q, cu_k, B, H, D, max_q, max_k, st);
+}
+
+int32_t attn_varlen_bwd_hostcu(const void* q, const void* k, const void* v, const void* o, const void* g,
+                               const float* lse, const int32_t* cu_q, const int32_t* cu_k, int32_t B, int32_t H,
+                               int32_t D, int32_t max_q, int32_t max_k, const attn_varlen_bwd_layout* st,
+                               float scale, uint32_t flags, float* delta, void* dq, void* dk, void* dv,
+                               void* stream) {
+    const int32_t rc =
+        attn_varlen_bwd_validate(q, k, v, o, g, lse, cu_q, cu_k, B, H, D, max_q, max_k, st, scale, flags, delta, dq,
+                                 dk, dv);
+    if (rc != ATTN_VARLEN_OK || B == 0) return rc;
+    return bwd_run(q, k, v, o, g, lse, cu_q, cu_k, B, H, D, st, scale, flags, delta, dq, dk, dv,
+                   static_cast<hipStream_t>(stream));
+}
+
+int32_t attn_varlen_bwd(const void* q, const void* k, const void* v, const void* o, const void* g, const float* lse,
+                        const int32_t* cu_q_dev, const int32_t* cu_k_dev, int32_t B, int32_t H, int32_t D,
+                        int32_t max_q, int32_t max_k, const attn_varlen_bwd_layout* st, float scale, uint32_t flags,
+                        float* delta, void* dq, void* dk, void* dv, void* stream) {
+    g_last_error.clear();
+    int32_t rc = bwd_check_scalars(q, k, v, o, g, lse, B, H, D, max_q, max_k, st, scale, flags, delta, dq, dk, dv);
+    if (rc != ATTN_VARLEN_OK || B == 0) return rc;
+    if (!cu_q_dev || !cu_k_dev) return fail(ATTN_VARLEN_ENULL, "cu_seqlens_q/k must be non-NULL");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    std::vector<int32_t> cu((size_t)2 * (B + 1));
+    hipError_t e = hipMemcpyAsync(cu.data(), cu_q_dev, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(cu.data() + B + 1, cu_k_dev, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "reading cu_seqlens failed: %s", hipGetErrorString(e));
+    const int32_t* cq = cu.data();
+    const int32_t* ck = cu.data() + B + 1;
+    rc = bwd_check_cu(cq, ck, B, H, D, max_q, max_k, st);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    return bwd_run(q, k, v, o, g, lse, cq, ck, B, H, D, st, scale, flags, delta, dq, dk, dv, s);
+}
+
+int32_t attn_varlen_bwd_grid_plan(const int32_t* cu_q, const int32_t* cu_k, int32_t B, int32_t H, int32_t D,
+                                  int64_t* pre_workgroups, int64_t* dkdv_workgroups, int64_t* dq_workgroups,
+                                  int64_t* launches) {
+    g_last_error.clear();
+    if (!cu_q || !cu_k || !pre_workgroups || !dkdv_workgroups || !dq_workgroups || !launches)
+        return fail(ATTN_VARLEN_ENULL, "NULL argument");
+    if (avf_bwd_block_n(D) <= 0) return fail(ATTN_VARLEN_EUNSUPPORTED, "head_dim %d not supported", D);
+    if (B < 0 || H <= 0) return fail(ATTN_VARLEN_EINVAL, "bad counts");
+    *pre_workgroups = *dkdv_workgroups = *dq_workgroups = *launches = 0;
+    if (B == 0) return ATTN_VARLEN_OK;
+    const int64_t items = (int64_t)cu_q[B] * H;
+    const int64_t chunk_rows = std::max<int64_t>(1, kPreItemsPerLaunch / H);
+    for (int64_t r0 = 0; r0 < cu_q[B]; r0 += chunk_rows)
+        *pre_workgroups += (std::min<int64_t>(chunk_rows, cu_q[B] - r0) * H + 15) / 16;
+    (void)items;
+    AvfBwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    auto none = [](const AvfBwdArgs&) { return hipSuccess; };
+    int32_t rc = for_each_launch(a, cu_q, cu_k, cu_k, B, H, avf_bwd_block_n(D), none, launches, dkdv_workgroups);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    return for_each_launch(a, cu_q, cu_k, cu_q, B, H, avf_bwd_block_m(D), none, launches, dq_workgroups);
+}
 
 }  // extern "C"

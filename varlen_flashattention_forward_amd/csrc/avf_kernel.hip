@@ -38,76 +38,16 @@
 
 #include <type_traits>
 
+#include "avf_device.h"
 #include "avf_plan.h"
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
+using namespace avf;
 
 // Largest per-lane partial row sum of softmax weights accepted before the
 // reference max is moved (bounds every weight by 2^16).
 constexpr float kPsumMax = 65536.0f;
-
-
-// gfx9 raw buffer descriptor word 3: 32-bit data format, no swizzle, no
-// index stride; records are bytes and out-of-range loads return 0.
-constexpr int kBufWord3 = 0x00020000;
-
-// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n and leaves the
-// export and LGKM counters untouched.
-__host__ __device__ constexpr int vmcnt_imm(int n) {
-    return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00;
-}
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             kBufWord3);
-}
-
-// 16-byte buffer load written straight to LDS: lane l of the wave fills LDS
-// bytes [lds_addr + 16*l, +16) (lds_addr in M0, wave-uniform) with the record at
-// `voffset` of the buffer resource `rsrc`. It is issued as inline assembly on
-// purpose: the compiler then does not track it, so it adds no vector-memory
-// waits of its own before later LDS reads (it would otherwise make every
-// transposing read wait for the loads of later stages, which write other
-// buffers of the ring). Completion is awaited explicitly with s_waitcnt vmcnt
-// and a barrier before the stage is read. Vector-memory loads complete in
-// order, so the compiler's own waits on older loads stay correct.
-__device__ inline void load_lds16(i32x4 rsrc, uint32_t lds_addr, uint32_t voffset) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(voffset), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
-                 : "memory");
-#endif
-}
-
-// Marks `x` as read and rewritten at this point of the instruction stream
-// (emits nothing). Between scheduling fences this keeps a pure arithmetic
-// result where the source computes it instead of letting the optimizer sink
-// it to its first use.
-template <typename V>
-__device__ inline void pin(V& x) {
-    asm volatile("" : "+v"(x));
-}
-
-// Buffer resource words (gfx9 layout) for the inline-assembly loads.
-__device__ inline i32x4 rsrc_words(const void* base, uint32_t bytes) {
-    const uint64_t b = (uint64_t)(uintptr_t)base;
-    i32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32) & 0xffff);  // stride 0
-    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-    r[3] = kBufWord3;
-    return r;
-}
 
 // LDS rows of K and V are unpadded (2*D bytes); the 16-byte chunks of a row are
 // permuted by XOR with a function of the key so that the MFMA fragment reads
@@ -405,15 +345,8 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     // V^T fragment u = k2 * DB + db of sub-block `sub` of the V buffer being read
     auto read_v = [&](int sub, int u) {
         const int k2 = u / T::DB, db = u % T::DB;
-        i16x4 half[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const char* p = lds + vcur[db] + sub * SUB + (k2 * 16 + r * 8) * T::ROWB;
-            half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
-        }
-        const i16x8 both = {half[0][0], half[0][1], half[0][2], half[0][3],
-                            half[1][0], half[1][1], half[1][2], half[1][3]};
-        return __builtin_bit_cast(bf16x8, both);
+        const char* p = lds + vcur[db] + sub * SUB + k2 * 16 * T::ROWB;
+        return read_tr8(p, p + 8 * T::ROWB);
     };
     // vsub: V sub-block g-1; ksub: K sub-block g+2 (refill_k false when there
     // is none), each in the buffer its address set points at

@@ -22,6 +22,10 @@ the pages' workloads are a private video model and a private training job):
 * ``causal_77k``: ``dense_77k`` with the causal mask (query row r of a segment
   sees keys j <= r + Lk - Lq); the pages only run causal=False, so this is an
   extension, with FLOPs counted over the visible (query, key) pairs.
+* ``bwd_9728``: the backward case of the _bwd_preprocess page ("Verified
+  sample", repro script): N=410923 in segments [0,225304,410923], H=16, D=96;
+  q, k, v one contiguous randn(3, N, H, D)*0.1 draw, dout (``make_dout``) an
+  [N, H, D] view with row stride 9728, N(0,1)*0.1 from its own seed.
 """
 from __future__ import annotations
 
@@ -114,6 +118,9 @@ WORKLOADS = {
                              0.1, True, layout="stride9728", outer_stride=9728),
     "dense_117k": Workload("dense_117k", 56, 128, (0, 117000), (0, 117000), 1.0, True),
     "causal_77k": Workload("causal_77k", 56, 128, (0, 77000), (0, 77000), 1.0, True, causal=True),
+    # backward: contiguous q, k, v; dout an [N, H, D] view of an [N, 9728] buffer (make_dout)
+    "bwd_9728": Workload("bwd_9728", 16, 96, (0, 225304, 410923), (0, 225304, 410923), 0.1, True,
+                         outer_stride=9728),
 }
 
 #: Canary written into the parts of an output buffer the kernel must not touch.
@@ -202,3 +209,26 @@ def sample_rows(w: Workload, per_segment: int, seed: int = 0, edge: int = 64) ->
         rows.extend(sorted(int(x) for x in pick))
         rows.extend(range(e - ed, e))
     return rows
+
+
+def make_dout(w: Workload, device="cuda", seed: int = 1, outer_stride: int = 0):
+    """Upstream gradient dout for the backward: bf16 N(0,1)*std drawn from its
+    own generator (seed `seed`). With outer_stride > 0 it is the [total_q, H, D]
+    view of columns [0, H*D) of an [total_q, outer_stride] buffer, the layout
+    a cat([attn_out, other], dim=1) hands to the attention backward (row
+    stride H*D + other width, 9728 on the _bwd_preprocess page); otherwise
+    contiguous. Returns (dout, base buffer)."""
+    H, D = w.num_heads, w.head_dim
+    n = w.total_q
+    g = _generator(device, seed)
+    if outer_stride:
+        if outer_stride < H * D:
+            raise ValueError("outer stride smaller than H*D")
+        base = torch.empty((n, outer_stride), dtype=torch.bfloat16, device=device)
+        base.normal_(generator=g)
+        base.mul_(w.std)
+        return base[:, : H * D].view(n, H, D), base
+    d = torch.randn((n, H, D), dtype=torch.bfloat16, device=device, generator=g)
+    if w.std != 1.0:
+        d.mul_(w.std)
+    return d, d
