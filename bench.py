@@ -2,6 +2,7 @@
 """Benchmark of the packed variable-length attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_77k]
+    python bench.py --backward [--workload bwd_9728]
 
 A step is one call of attn_varlen_fwd through the C ABI with cu_seqlens on the
 device: the cu read-back, the exact tile plan and the kernel launch. Inputs are
@@ -9,6 +10,12 @@ resident in HBM before timing starts. Prints ONE JSON line on stdout:
 TFLOP/s with FLOPs = sum over segments of 4*Lq*Lk*D*H, the kernel's roofline
 figures (its own average duration from HIP events on the launch stream), and
 the CPU oracle's throughput on a bounded sample of the same workload.
+
+With --backward a step is one attn_varlen_bwd call (device cu_seqlens): the
+preprocessing pass, the dK/dV kernel and the dQ kernel, on the dout layout of
+the _bwd_preprocess page (row stride 9728). FLOPs follow the flash-attention
+convention for the backward, 10*Lq*Lk*D*H per segment (five matrix products
+of the forward's size; the kernels form S and dP twice, so they execute 14).
 """
 from __future__ import annotations
 
@@ -72,14 +79,131 @@ def cpu_baseline(w, t, rows_per_segment: int):
                       f"{'visible ' if w.causal else ''}segments (C fp64 oracle, {dt:.1f} s, {flops / 1e9:.1f} GFLOP)"}
 
 
+def cpu_baseline_bwd(w, t, dout, rows_per_segment: int):
+    import numpy as np
+
+    import oracle
+    from varlen_flashattention_forward_amd.workloads import sample_rows
+
+    rows = sample_rows(w, rows_per_segment, edge=min(4, rows_per_segment // 2))
+    q, k, v = (t[n].contiguous().cpu() for n in ("q", "k", "v"))
+    g = dout.contiguous().cpu()
+    threads = oracle.default_threads()
+    # a dq row forms S, dP and dQ against its segment's keys: 3 of the 5 products
+    flops = sum(6 * w.visible_keys(r) * w.head_dim * w.num_heads for r in rows)
+    t0 = time.perf_counter()
+    oracle.attn_varlen_bwd_dq_rows(q, k, v, g, w.cu_q, w.cu_k, float(np.float32(w.softmax_scale)), rows,
+                                   causal=w.causal, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"dq of {len(rows)} query rows x {w.num_heads} heads of {w.name} against their "
+                      f"segments (C fp64 oracle, {dt:.1f} s, {flops / 1e9:.1f} GFLOP counted as 6*Lk*D*H "
+                      f"per row: S, dP and dQ)"}
+
+
+def bench_backward(args) -> int:
+    import torch
+
+    import varlen_flashattention_forward_amd as avf
+    from varlen_flashattention_forward_amd.workloads import WORKLOADS, make_dout, make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    avf.lib()
+    log(f"[bench-bwd] workload {w.name}: H={w.num_heads} D={w.head_dim} segments={w.num_segments} "
+        f"total_q={w.total_q} dout row stride {w.outer_stride or 'contiguous'}")
+    t = make_inputs(w, dev, seed=0)
+    dout, _ = make_dout(w, dev, seed=1, outer_stride=w.outer_stride)
+    out, lse = avf.attn_varlen_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                                   softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"], causal=w.causal)
+    dq = torch.empty_like(t["q"], memory_format=torch.contiguous_format)
+    dk = torch.empty_like(t["k"], memory_format=torch.contiguous_format)
+    dv = torch.empty_like(t["v"], memory_format=torch.contiguous_format)
+    delta = torch.empty((w.num_heads, w.total_q), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    flops = w.flops() // 4 * 10
+    stream = torch.cuda.current_stream(dev)
+
+    def step(**kw):
+        avf.attn_varlen_bwd(t["q"], t["k"], t["v"], out, dout, lse, t["cu_q"], t["cu_k"], w.max_seqlen_q,
+                            w.max_seqlen_k, softmax_scale=w.softmax_scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
+                            delta=delta, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench-bwd] warmup done ({args.warmup} steps)")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    value = flops / (ms / 1e3) / 1e12
+    log(f"[bench-bwd] {args.steps} steps: {ms:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    # the pass's kernels alone: HIP events on the launch stream around the
+    # synchronisation-free entry point (three kernels back to back)
+    cu_q, cu_k = list(w.cu_q), list(w.cu_k)
+    durs = []
+    for _ in range(args.steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step(cu_seqlens_q_host=cu_q, cu_seqlens_k_host=cu_k, stream=stream.cuda_stream)
+        e1.record(stream)
+        durs.append((e0, e1))
+    torch.cuda.synchronize()
+    kms = sum(a.elapsed_time(b) for a, b in durs) / len(durs)
+    pre_wg, dkdv_wg, dq_wg, launches = avf.bwd_grid_plan(w.cu_q, w.cu_k, w.num_heads, w.head_dim)
+    achieved = flops / (kms / 1e3) / 1e12
+    log(f"[bench-bwd] kernels: {kms:.3f} ms/call, {achieved:.1f} TFLOP/s; workgroups pre {pre_wg} "
+        f"dkdv {dkdv_wg} dq {dq_wg}")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "backward pass: avf_bwd_pre_kernel + avf_bwd_dkdv_kernel + avf_bwd_dq_kernel",
+                "kernel_ms": round(kms, 4), "algorithmic_flops_per_launch": flops,
+                "executed_mfma_flops_per_launch": flops // 10 * 14}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench-bwd] CPU oracle baseline ...")
+        cpu = cpu_baseline_bwd(w, t, dout, args.cpu_rows_bwd)
+        log(f"[bench-bwd] cpu baseline {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+    rec = {
+        "metric": "attention bwd TFLOP/s (10*Sq*Sk*D*H) and % of MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": w.name, "pass": "backward", "num_heads": w.num_heads, "head_dim": w.head_dim,
+                   "segments": w.num_segments, "total_q": w.total_q, "total_k": w.total_k,
+                   "dout_row_stride": dout.stride(0), "causal": w.causal, "flops_per_step": flops,
+                   "workgroups": {"preprocess": pre_wg, "dkdv": dkdv_wg, "dq": dq_wg}},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dense_77k")
+    ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-rows", type=int, default=160, help="query rows per segment for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true", help="time the backward pass (default workload bwd_9728)")
+    ap.add_argument("--cpu-rows-bwd", type=int, default=8, help="dq rows per segment for the backward CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (scales HBM counters)")
     args = ap.parse_args()
@@ -87,6 +211,10 @@ def main() -> int:
         print(f"bench.py measures one GPU only: the library runs on a single MI355X and has no "
               f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         return 2
+    if args.workload is None:
+        args.workload = "bwd_9728" if args.backward else "dense_77k"
+    if args.backward:
+        return bench_backward(args)
 
     import torch
 
