@@ -202,6 +202,8 @@ def main() -> int:
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-rows", type=int, default=160, help="query rows per segment for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--async", dest="use_async", action="store_true",
+                    help="time the sync-free entry point (device planner, no host read-back)")
     ap.add_argument("--backward", action="store_true", help="time the backward pass (default workload bwd_9728)")
     ap.add_argument("--cpu-rows-bwd", type=int, default=8, help="dq rows per segment for the backward CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -241,9 +243,16 @@ def main() -> int:
     flops = w.flops()
     stream = torch.cuda.current_stream(dev)
 
+    ws = avf.async_workspace(w.num_segments, dev) if args.use_async else None
+
     def step():
-        avf.attn_varlen_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
-                            softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"], causal=w.causal)
+        if args.use_async:
+            avf.attn_varlen_fwd_async(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                                      workspace=ws, softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"],
+                                      causal=w.causal)
+        else:
+            avf.attn_varlen_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                                softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"], causal=w.causal)
 
     for _ in range(args.warmup):
         step()
@@ -266,15 +275,20 @@ def main() -> int:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        avf.attn_varlen_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
-                            softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"],
-                            cu_seqlens_q_host=cu_q, cu_seqlens_k_host=cu_k, stream=stream.cuda_stream,
-                            causal=w.causal)
+        if args.use_async:
+            step()  # planner + attention kernel on the current stream
+        else:
+            avf.attn_varlen_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                                softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"],
+                                cu_seqlens_q_host=cu_q, cu_seqlens_k_host=cu_k, stream=stream.cuda_stream,
+                                causal=w.causal)
         e1.record(stream)
         durs.append((e0, e1))
     torch.cuda.synchronize()
     kms = sum(a.elapsed_time(b) for a, b in durs) / len(durs)
     launches, wgs = avf.grid_plan(w.cu_q, w.num_heads, w.head_dim)
+    if args.use_async:
+        launches, wgs = 1, avf.async_grid(w.total_q, w.num_segments, w.num_heads, w.head_dim, w.max_seqlen_q)
     achieved = flops / launches / (kms / launches / 1e3) / 1e12
     log(f"[bench] kernel: {kms:.3f} ms/call over {launches} launch(es), {wgs} workgroups, {achieved:.1f} TFLOP/s")
     traffic = traffic_for(w.name)
@@ -307,7 +321,8 @@ def main() -> int:
                    "segments": w.num_segments, "total_q": w.total_q, "total_k": w.total_k,
                    "max_seqlen_q": w.max_seqlen_q, "max_seqlen_k": w.max_seqlen_k,
                    "layout": w.layout, "causal": w.causal, "flops_per_step": flops,
-                   "workgroups": wgs, "block_m": avf.block_m(w.head_dim)},
+                   "workgroups": wgs, "block_m": avf.block_m(w.head_dim),
+                   "entry": "attn_varlen_fwd_async" if args.use_async else "attn_varlen_fwd"},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

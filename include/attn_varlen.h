@@ -250,6 +250,58 @@ int32_t attn_fwd_batched_validate(const void* q, const void* k, const void* v, i
                                   const float* lse);
 
 /*
+ * ---- Sync-free forward (device planner) ------------------------------------
+ *
+ * attn_varlen_fwd with device cu_seqlens and NO host synchronisation: the
+ * call enqueues two kernels on `stream` and returns. Why: the FA4 SM120 page
+ * stresses the kernel's speed on small inputs ("~7x faster than our fallback
+ * for small inputs") where a per-call device-to-host read-back of cu_seqlens
+ * costs as much as the attention itself, and a call without host waits can be
+ * captured in a HIP graph.
+ *   1. A one-workgroup planner kernel checks cu_seqlens on the device (start
+ *      at 0, non-decreasing, segments within max_seqlen_q/k, ends within
+ *      q_tokens/k_tokens) and writes the tile prefix into `workspace`.
+ *   2. The attention kernel is launched on a grid sized from host-known values
+ *      only: at most H * min(ceil((q_tokens + B*(BM-1)) / BM), B*ceil(max_seqlen_q
+ *      / BM)) tiles exist (the first term is the SM120 page's grid formula,
+ *      "Interpretation"), capped at 8192 workgroups (a multiple of 8). Each
+ *      workgroup first reads the planner's status and real tile count, forms
+ *      no address for any tile at or past that count (the page's suggested
+ *      fix: gate the tile prologue on validity), and loops over tiles
+ *      w, w + grid, ... when the count exceeds the grid. One launch serves any
+ *      number of segments.
+ * Arguments as attn_varlen_fwd_ex, plus:
+ *   workspace        device buffer of attn_varlen_async_workspace_bytes(B)
+ *                    bytes, 16-byte aligned, owned by the caller; overwritten
+ *                    by every call (calls that share one workspace must be
+ *                    ordered on one stream).
+ *   workspace_bytes  its size.
+ * Host-side argument errors are returned as usual. Errors in the cu_seqlens
+ * VALUES cannot be returned (the host never sees them): the planner stores
+ * ATTN_VARLEN_ECU / ATTN_VARLEN_EMAXSEQ / ATTN_VARLEN_EUNSUPPORTED (tile count
+ * >= 2^31) in the workspace's first int32 word, 0 when valid, and the
+ * attention kernel then writes nothing. attn_varlen_async_status reads it.
+ * Since total_q is unknown on the host, out must not overlap itself over
+ * q_tokens rows and a non-zero lse_head must be >= q_tokens when H > 1.
+ */
+int64_t attn_varlen_async_workspace_bytes(int32_t num_segments);
+
+int32_t attn_varlen_fwd_async(const void* q, const void* k, const void* v,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t num_segments, int32_t num_heads, int32_t head_dim,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              const attn_varlen_layout* layout, float softmax_scale, uint32_t flags,
+                              void* workspace, int64_t workspace_bytes, void* out, float* lse,
+                              void* stream);
+
+/* Copy the workspace's status word to *status (waits for `stream`). */
+int32_t attn_varlen_async_status(const void* workspace, void* stream, int32_t* status);
+
+/* Workgroups attn_varlen_fwd_async launches for these host-known values. */
+int32_t attn_varlen_async_grid(int64_t q_tokens, int32_t num_segments, int32_t num_heads,
+                               int32_t head_dim, int32_t max_seqlen_q, int64_t* workgroups);
+
+/*
  * ---- Backward -------------------------------------------------------------
  *
  * Gradients of the varlen forward above for an upstream gradient

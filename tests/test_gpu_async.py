@@ -1,0 +1,164 @@
+"""GPU tests of the sync-free forward (device planner + bounded, looping
+grid): bitwise agreement with the host-planned path, one launch for any
+number of segments, invalid cu_seqlens values reported through the
+workspace status with the outputs untouched, and capture in a HIP graph.
+Marked `gpu`; every case prints its name before it touches the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import varlen_flashattention_forward_amd as avf
+from varlen_flashattention_forward_amd import _binding
+from varlen_flashattention_forward_amd.workloads import CANARY, custom, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(label):
+    print(f"\n[gpu-case] {label}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    avf.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def host_planned(t, w, causal=False):
+    o = torch.full_like(t["out"], CANARY)
+    l = torch.full_like(t["lse"], CANARY)
+    avf.attn_varlen_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                        softmax_scale=w.softmax_scale, out=o, lse=l, causal=causal,
+                        cu_seqlens_q_host=list(w.cu_q), cu_seqlens_k_host=list(w.cu_k))
+    return o, l
+
+
+def sync_free(t, w, causal=False, ws=None, max_q=None, max_k=None):
+    o = torch.full_like(t["out"], CANARY)
+    l = torch.full_like(t["lse"], CANARY)
+    _, _, ws = avf.attn_varlen_fwd_async(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"],
+                                         w.max_seqlen_q if max_q is None else max_q,
+                                         w.max_seqlen_k if max_k is None else max_k, workspace=ws,
+                                         softmax_scale=w.softmax_scale, out=o, lse=l, causal=causal)
+    return o, l, ws
+
+
+def random_cu(rng, B, max_len, empty_frac=0.15):
+    lens = [0 if rng.random() < empty_frac else int(rng.integers(1, max_len + 1)) for _ in range(B)]
+    return np.concatenate([[0], np.cumsum(lens)]).astype(int).tolist()
+
+
+CASES = {
+    # (H, D, cu_q, cu_k)
+    "cross_d128": (4, 128, [0, 4032, 9072, 9100, 10000], [0, 1758, 3516, 5274, 7032]),
+    "ragged_d96": (3, 96, [0, 1, 300, 300, 813, 1100], [0, 70, 71, 104, 744, 873]),
+    "self_d64": (2, 64, [0, 255, 256, 700], None),
+}
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_sync_free_equals_host_planned(name, causal):
+    H, D, cu_q, cu_k = CASES[name]
+    announce(f"sync-free {name} causal={causal}")
+    w = custom(name, H, D, cu_q, cu_k, std=1.0)
+    t = make_inputs(w, "cuda", seed=1)
+    a_o, a_l = host_planned(t, w, causal)
+    b_o, b_l, ws = sync_free(t, w, causal)
+    torch.cuda.synchronize()
+    assert avf.async_status(ws) == 0
+    assert torch.equal(a_o, b_o)
+    assert torch.equal(a_l[:, :w.total_q], b_l[:, :w.total_q])
+
+
+def test_sync_free_many_segments_one_launch():
+    """300 segments (the host-planned path splits them over launches of 128)."""
+    announce("sync-free 300 segments")
+    rng = np.random.default_rng(2)
+    cu_q = random_cu(rng, 300, 200)
+    cu_k = random_cu(rng, 300, 150)
+    w = custom("many", 2, 64, cu_q, cu_k, std=1.0)
+    t = make_inputs(w, "cuda", seed=2)
+    a_o, a_l = host_planned(t, w)
+    b_o, b_l, ws = sync_free(t, w)
+    torch.cuda.synchronize()
+    assert avf.async_status(ws) == 0
+    assert torch.equal(a_o, b_o) and torch.equal(a_l[:, :w.total_q], b_l[:, :w.total_q])
+
+
+def test_sync_free_grid_smaller_than_tile_count_loops():
+    """More tiles than the 8192-workgroup cap: workgroups take several tiles."""
+    announce("sync-free looping grid")
+    w = custom("loop", 64, 64, [0, 33000], std=1.0)
+    bm = avf.block_m(64)
+    assert avf.count_tiles(w.cu_q, 64, bm) > avf.async_grid(w.total_q, 1, 64, 64, w.max_seqlen_q) == 8192
+    t = make_inputs(w, "cuda", seed=3)
+    a_o, a_l = host_planned(t, w)
+    b_o, b_l, ws = sync_free(t, w)
+    torch.cuda.synchronize()
+    assert avf.async_status(ws) == 0
+    assert torch.equal(a_o, b_o) and torch.equal(a_l[:, :w.total_q], b_l[:, :w.total_q])
+
+
+@pytest.mark.parametrize("bad", ["decreasing", "past_tokens", "over_max_q", "nonzero_start"])
+def test_sync_free_reports_bad_cu_and_writes_nothing(bad):
+    announce(f"sync-free bad cu {bad}")
+    w = custom("bad", 2, 64, [0, 100, 300], [0, 120, 250], std=1.0)
+    t = make_inputs(w, "cuda", seed=4)
+    cq, ck = list(w.cu_q), list(w.cu_k)
+    max_q = None
+    if bad == "decreasing":
+        ck = [0, 200, 150]
+        expect = _binding.ECU
+    elif bad == "past_tokens":
+        cq = [0, 100, 301]
+        expect = _binding.ECU
+    elif bad == "over_max_q":
+        max_q = 150
+        expect = _binding.EMAXSEQ
+    else:
+        cq = [5, 100, 300]
+        expect = _binding.ECU
+    t["cu_q"] = torch.tensor(cq, dtype=torch.int32, device="cuda")
+    t["cu_k"] = torch.tensor(ck, dtype=torch.int32, device="cuda")
+    o, l, ws = sync_free(t, w, max_q=max_q)
+    torch.cuda.synchronize()
+    assert avf.async_status(ws) == expect
+    assert bool((o == CANARY).all()) and bool((l == CANARY).all())
+
+
+def test_sync_free_in_a_hip_graph():
+    """Capture one sync-free call, replay it on new inputs several times with
+    eager work between replays; every replay equals the host-planned result."""
+    announce("sync-free graph capture")
+    w = custom("graph", 4, 128, [0, 700, 1500, 1501], [0, 400, 1200, 1900], std=1.0)
+    t = make_inputs(w, "cuda", seed=5)
+    ws = avf.async_workspace(w.num_segments, "cuda")
+    o = torch.empty_like(t["out"])
+    l = torch.empty_like(t["lse"])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        # warm-up call outside capture
+        avf.attn_varlen_fwd_async(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                                  workspace=ws, out=o, lse=l)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        avf.attn_varlen_fwd_async(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                                  workspace=ws, out=o, lse=l)
+    for rep in range(3):
+        gen = torch.Generator(device="cuda").manual_seed(100 + rep)
+        t["q"].copy_(torch.randn(t["q"].shape, dtype=torch.bfloat16, device="cuda", generator=gen))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_o, ref_l = host_planned(t, w)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o), rep
+        assert torch.equal(l[:, :w.total_q], ref_l[:, :w.total_q]), rep

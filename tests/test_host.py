@@ -275,3 +275,123 @@ def test_batched_validate_accepts():
 ])
 def test_batched_validate_rejects(kwargs, code):
     assert vb(**kwargs) == code
+
+
+# ---------------------------------------------------------------- backward (host checks only)
+
+def bwd_layout(H=2, D=64, nq=10, nk=12, **kw):
+    hd = H * D
+    base = dict(q_row=hd, q_head=D, k_row=hd, k_head=D, v_row=hd, v_head=D, o_row=hd, o_head=D,
+                do_row=hd, do_head=D, dq_row=hd, dq_head=D, dk_row=hd, dk_head=D, dv_row=hd, dv_head=D,
+                lse_head=0, delta_head=0, q_tokens=nq, k_tokens=nk)
+    base.update(kw)
+    return _binding.BwdLayout(**base)
+
+
+def vb_bwd(cu_q=(0, 4, 10), cu_k=(0, 5, 12), H=2, D=64, max_q=6, max_k=7, lay=None, scale=0.125, flags=0,
+           ptrs=None, **repl):
+    names = ("q", "k", "v", "out", "dout", "lse", "delta", "dq", "dk", "dv")
+    p = dict(zip(names, [P] * 10))
+    p.update(ptrs or {})
+    return avf.validate_bwd(tuple(p[n] for n in names), list(cu_q), list(cu_k), H, D, max_q, max_k,
+                            lay or bwd_layout(H, D, **repl), scale, flags)
+
+
+def test_bwd_validate_accepts():
+    assert vb_bwd() == 0
+    assert vb_bwd(flags=avf.CAUSAL) == 0
+    assert vb_bwd(D=96, lay=bwd_layout(D=96)) == 0
+    # the page's dout view: row stride 9728
+    assert vb_bwd(H=16, D=96, lay=bwd_layout(H=16, D=96, do_row=9728, do_head=96)) == 0
+    assert vb_bwd(cu_q=(0,), cu_k=(0,)) == 0  # no segments
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(ptrs={"dout": None}), _binding.ENULL),
+    (dict(ptrs={"delta": None}), _binding.ENULL),
+    (dict(ptrs={"dk": None}), _binding.ENULL),
+    (dict(ptrs={"dq": P + 8}), _binding.EALIGN),
+    (dict(ptrs={"lse": P + 2}), _binding.EALIGN),
+    (dict(do_row=100), _binding.EALIGN),
+    (dict(dq_row=0), _binding.EINVAL),
+    (dict(dk_head=-8), _binding.EINVAL),
+    (dict(dv_row=8, dv_head=8), _binding.EINVAL),            # dv rows overlap
+    (dict(delta_head=8), _binding.EINVAL),                   # delta rows of head 1 overlap head 0
+    (dict(lse_head=4), _binding.EINVAL),
+    (dict(do_row=1 << 23), _binding.EUNSUPPORTED),
+    (dict(D=80), _binding.EUNSUPPORTED),
+    (dict(flags=2), _binding.EINVAL),
+    (dict(nq=9), _binding.ECU),                              # cu ends past q_tokens
+    (dict(cu_k=(0, 5, 4)), _binding.ECU),                   # decreasing
+    (dict(max_k=4), _binding.EMAXSEQ),
+    (dict(scale=0.0), _binding.EINVAL),
+])
+def test_bwd_validate_rejects(kwargs, code):
+    D = kwargs.pop("D", 64)
+    assert vb_bwd(D=D, **kwargs) == code
+
+
+def test_bwd_grid_plan_counts_key_and_row_blocks():
+    pre, dkdv, dq, launches = avf.bwd_grid_plan([0, 225304, 410923], [0, 225304, 410923], 16, 96)
+    assert pre == 410923 * 16 // 16
+    assert dkdv == 16 * (math.ceil(225304 / 128) + math.ceil(185619 / 128)) == dq
+    assert launches == 2
+    # cross attention: dK/dV tiles follow the key lengths, dQ tiles the query lengths
+    pre, dkdv, dq, launches = avf.bwd_grid_plan([0, 5, 5, 300], [0, 0, 7, 7], 3, 128)
+    assert (dkdv, dq) == (3 * 1, 3 * (1 + 3)) and pre == math.ceil(300 * 3 / 16)
+
+
+def test_bwd_preprocess_rejects_before_any_hip_call():
+    L = avf.lib()
+    assert L.attn_varlen_bwd_preprocess(P, None, 10, 2, 64, 128, 64, 128, 64, P, 10, None) == _binding.ENULL
+    assert L.attn_varlen_bwd_preprocess(P, P, 10, 2, 64, 128, 64, 128, 64, P, 5, None) == _binding.EINVAL
+    assert L.attn_varlen_bwd_preprocess(P, P, 10, 2, 80, 128, 64, 128, 64, P, 10, None) == _binding.EUNSUPPORTED
+    assert L.attn_varlen_bwd_preprocess(P, P, 0, 2, 64, 128, 64, 128, 64, P, 10, None) == 0  # no rows
+
+
+# ---------------------------------------------------------------- sync-free forward (host side)
+
+@pytest.mark.parametrize("seed", range(5))
+def test_async_grid_bounds_the_tile_count(seed):
+    """The host-only grid covers every tile for any cu consistent with
+    q_tokens and max_seqlen_q (or loops over them at the cap)."""
+    rng = random.Random(seed)
+    for _ in range(50):
+        B = rng.randint(1, 300)
+        lens = [rng.choice([0, 1, rng.randint(1, 3000)]) for _ in range(B)]
+        cu = [0]
+        for x in lens:
+            cu.append(cu[-1] + x)
+        H, D = rng.choice([1, 3, 56]), rng.choice([64, 96, 128])
+        q_tokens = cu[-1] + rng.randint(0, 500)
+        max_q = max(lens) + rng.randint(0, 100)
+        bm = avf.block_m(D)
+        tiles = avf.count_tiles(cu, H, bm)
+        g = avf.async_grid(q_tokens, B, H, D, max_q)
+        assert g % 8 == 0 and g <= 8192
+        assert g >= min(tiles, 8192)
+        bound = H * min(math.ceil((q_tokens + B * (bm - 1)) / bm), B * math.ceil(max_q / bm))
+        assert tiles <= bound and g == min(8192, -(-bound // 8) * 8)
+
+
+def test_async_workspace_bytes():
+    assert avf.async_workspace_bytes(0) == 256
+    assert avf.async_workspace_bytes(2) == 256
+    assert avf.async_workspace_bytes(1000) == -(-(4 * (4 + 1001)) // 256) * 256
+    with pytest.raises(avf.AttnVarlenError):
+        avf.async_workspace_bytes(-1)
+
+
+def test_async_rejects_host_errors_before_any_hip_call():
+    L = avf.lib()
+    lay = layout()
+    cq = P
+    args = lambda ws, nbytes, flags=0: (P, P, P, cq, cq, 2, 2, 64, 6, 7, ctypes.byref(lay), 0.125, flags, ws, nbytes,
+                                        P, P, None)
+    assert L.attn_varlen_fwd_async(*args(None, 256)) == _binding.ENULL
+    assert L.attn_varlen_fwd_async(*args(P + 4, 256)) == _binding.EALIGN
+    assert L.attn_varlen_fwd_async(*args(P, 16)) == _binding.EINVAL
+    assert L.attn_varlen_fwd_async(*args(P, 256, flags=4)) == _binding.EINVAL
+    lay_bad = layout(o_row=8, o_head=8)
+    bad = (P, P, P, cq, cq, 2, 2, 64, 6, 7, ctypes.byref(lay_bad), 0.125, 0, P, 256, P, P, None)
+    assert L.attn_varlen_fwd_async(*bad) == _binding.EINVAL

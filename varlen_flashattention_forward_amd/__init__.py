@@ -6,7 +6,8 @@ kernels behind the C ABI of include/attn_varlen.h (libattn_varlen.so). This
 package is the thin Python binding over it.
 """
 from ._binding import (  # noqa: F401
-    CAUSAL, AttnVarlenError, BatchedLayout, BwdLayout, Layout, attn_fwd, attn_varlen_bwd, attn_varlen_fwd,
+    CAUSAL, AttnVarlenError, BatchedLayout, BwdLayout, Layout, async_grid, async_status, async_workspace,
+    async_workspace_bytes, attn_fwd, attn_varlen_bwd, attn_varlen_fwd, attn_varlen_fwd_async,
     block_m, bwd_grid_plan, bwd_preprocess, count_tiles, decode_tile, element_offset, grid_plan, last_error, lib,
     segments_per_launch, validate, validate_batched, validate_bwd,
 )

@@ -27,7 +27,8 @@ EXPORTED_SYMBOLS = (
     "attn_varlen_fwd_ex", "attn_varlen_fwd_hostcu_ex", "attn_varlen_validate_ex",
     "attn_fwd_batched", "attn_fwd_batched_validate",
     "attn_varlen_bwd_preprocess", "attn_varlen_bwd", "attn_varlen_bwd_hostcu", "attn_varlen_bwd_validate",
-    "attn_varlen_bwd_grid_plan",
+    "attn_varlen_bwd_grid_plan", "attn_varlen_async_workspace_bytes", "attn_varlen_fwd_async",
+    "attn_varlen_async_status", "attn_varlen_async_grid",
 )
 
 CAUSAL = 1  # ATTN_VARLEN_CAUSAL
@@ -108,6 +109,14 @@ def lib():
         L.attn_varlen_bwd_grid_plan.restype = ctypes.c_int32
         L.attn_varlen_bwd_grid_plan.argtypes = [_i32p, _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                 _i64p, _i64p, _i64p, _i64p]
+        L.attn_varlen_async_workspace_bytes.restype = ctypes.c_int64
+        L.attn_varlen_async_workspace_bytes.argtypes = [ctypes.c_int32]
+        L.attn_varlen_fwd_async.restype = ctypes.c_int32
+        L.attn_varlen_fwd_async.argtypes = fwd_args[:12] + [ctypes.c_uint32, _vp, ctypes.c_int64] + fwd_args[12:]
+        L.attn_varlen_async_status.restype = ctypes.c_int32
+        L.attn_varlen_async_status.argtypes = [_vp, _vp, _i32p]
+        L.attn_varlen_async_grid.restype = ctypes.c_int32
+        L.attn_varlen_async_grid.argtypes = [ctypes.c_int64] + [ctypes.c_int32] * 4 + [_i64p]
         L.attn_varlen_block_m.restype = ctypes.c_int32
         L.attn_varlen_block_m.argtypes = [ctypes.c_int32]
         L.attn_varlen_count_tiles.restype = ctypes.c_int64
@@ -273,6 +282,87 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
                                   out.data_ptr(), lse_ptr, stream)
     _check(rc)
     return out, lse
+
+
+def async_workspace_bytes(num_segments: int) -> int:
+    r = lib().attn_varlen_async_workspace_bytes(num_segments)
+    if r < 0:
+        _check(int(r))
+    return int(r)
+
+
+def async_grid(q_tokens: int, num_segments: int, num_heads: int, head_dim: int, max_seqlen_q: int) -> int:
+    g = ctypes.c_int64()
+    _check(lib().attn_varlen_async_grid(q_tokens, num_segments, num_heads, head_dim, max_seqlen_q,
+                                        ctypes.byref(g)))
+    return g.value
+
+
+def async_workspace(num_segments: int, device):
+    """A workspace tensor for attn_varlen_fwd_async (caller-owned device memory)."""
+    import torch
+
+    return torch.empty(async_workspace_bytes(num_segments) // 4, dtype=torch.int32, device=device)
+
+
+def async_status(workspace, stream=None) -> int:
+    """The planner's status word of the last call that used `workspace` (waits for the stream)."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(workspace.device).cuda_stream
+    st = ctypes.c_int32()
+    _check(lib().attn_varlen_async_status(workspace.data_ptr(), stream, ctypes.byref(st)))
+    return st.value
+
+
+def attn_varlen_fwd_async(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                          workspace=None, softmax_scale: float | None = None, out=None, lse=None,
+                          return_lse: bool = True, stream=None, causal: bool = False):
+    """Sync-free varlen attention forward (device planner; no host wait).
+
+    Same tensors as attn_varlen_fwd; cu_seqlens_q/k must be int32 device
+    tensors. `workspace` (from async_workspace) is allocated when not given.
+    Errors in the cu values are reported through async_status(workspace).
+    Returns (out, lse, workspace).
+    """
+    import torch
+
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
+    total_q, H, D = q.shape
+    if k.shape[1:] != (H, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [total_k, H, D] matching q's H and D")
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if cu.dtype != torch.int32 or not cu.is_cuda or cu.dim() != 1 or not cu.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    B = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((total_q, H, D), dtype=torch.bfloat16, device=q.device)
+    lse_head = 0
+    if lse is None and return_lse:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        if lse.dtype != torch.float32 or lse.dim() != 2 or lse.shape[0] != H or lse.stride(1) != 1 \
+                or lse.shape[1] < total_q:
+            raise ValueError("lse must be fp32 [H, >= total_q] with unit inner stride")
+        lse_head = lse.stride(0)
+    if workspace is None:
+        workspace = async_workspace(B, q.device)
+    layout = _layout_of(q, k, v, out, lse, lse_head)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().attn_varlen_fwd_async(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
+                                     cu_seqlens_k.data_ptr(), B, H, D, int(max_seqlen_q), int(max_seqlen_k),
+                                     ctypes.byref(layout), float(softmax_scale), CAUSAL if causal else 0,
+                                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                     out.data_ptr(), lse.data_ptr() if lse is not None else None, stream)
+    _check(rc)
+    return out, lse, workspace
 
 
 def attn_fwd(q, k, v, softmax_scale: float | None = None, causal: bool = False, out=None, lse=None,

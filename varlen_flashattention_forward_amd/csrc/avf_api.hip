@@ -733,3 +733,117 @@ int32_t attn_varlen_bwd_grid_plan(const int32_t* cu_q, const int32_t* cu_k, int3
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Sync-free forward: device planner + bounded, looping grid
+
+namespace {
+
+// Workgroups of a device-planned launch: at most this many (a multiple of 8;
+// larger problems loop), and never more than the bound on the tile count.
+constexpr int64_t kAsyncMaxGrid = 8192;
+
+int64_t async_workspace_bytes(int32_t B) {
+    const int64_t bytes = 4 * ((int64_t)AVF_PLAN_HEADER_WORDS + B + 1);
+    return (bytes + 255) / 256 * 256;
+}
+
+// Upper bound on H * sum_b ceil(Lq_b / bm) from host-known values only:
+// sum_b ceil(Lq_b / bm) <= ceil((total_q + B * (bm - 1)) / bm) with
+// total_q <= q_tokens (the SM120 page's grid formula), and <= B * ceil(max_q / bm).
+int64_t async_tile_bound(int64_t q_tokens, int32_t B, int32_t H, int32_t bm, int32_t max_q) {
+    const int64_t a = (q_tokens + (int64_t)B * (bm - 1) + bm - 1) / bm;
+    const int64_t b = (int64_t)B * ((max_q + bm - 1) / bm);
+    return (int64_t)H * std::min(a, b);
+}
+
+int64_t async_grid(int64_t bound) {
+    const int64_t g = std::min(bound, kAsyncMaxGrid);
+    return (g + AVF_NUM_XCD - 1) / AVF_NUM_XCD * AVF_NUM_XCD;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t attn_varlen_async_workspace_bytes(int32_t B) {
+    g_last_error.clear();
+    if (B < 0) return fail(ATTN_VARLEN_EINVAL, "num_segments must be >= 0 (got %d)", B);
+    return async_workspace_bytes(B);
+}
+
+int32_t attn_varlen_async_grid(int64_t q_tokens, int32_t B, int32_t H, int32_t D, int32_t max_q,
+                               int64_t* workgroups) {
+    g_last_error.clear();
+    if (!workgroups) return fail(ATTN_VARLEN_ENULL, "NULL argument");
+    const int32_t bm = avf_block_m(D);
+    if (bm <= 0) return fail(ATTN_VARLEN_EUNSUPPORTED, "head_dim %d not supported", D);
+    if (B < 0 || H <= 0 || q_tokens < 0 || max_q < 0) return fail(ATTN_VARLEN_EINVAL, "bad counts");
+    *workgroups = async_grid(async_tile_bound(q_tokens, B, H, bm, max_q));
+    return ATTN_VARLEN_OK;
+}
+
+int32_t attn_varlen_fwd_async(const void* q, const void* k, const void* v, const int32_t* cu_q_dev,
+                              const int32_t* cu_k_dev, int32_t B, int32_t H, int32_t D, int32_t max_q,
+                              int32_t max_k, const attn_varlen_layout* st, float scale, uint32_t flags,
+                              void* workspace, int64_t workspace_bytes, void* out, float* lse, void* stream) {
+    g_last_error.clear();
+    int32_t rc = check_flags(flags);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    rc = check_scalars(q, k, v, B, H, D, max_q, max_k, st, scale, out, lse);
+    if (rc != ATTN_VARLEN_OK || B == 0) return rc;
+    if (!cu_q_dev || !cu_k_dev) return fail(ATTN_VARLEN_ENULL, "cu_seqlens_q/k must be non-NULL");
+    if (!workspace) return fail(ATTN_VARLEN_ENULL, "workspace must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 15u) return fail(ATTN_VARLEN_EALIGN, "workspace must be 16-byte aligned");
+    if (workspace_bytes < async_workspace_bytes(B))
+        return fail(ATTN_VARLEN_EINVAL, "workspace of %lld bytes is smaller than the %lld needed",
+                    (long long)workspace_bytes, (long long)async_workspace_bytes(B));
+    // the checks that need cu, with q_tokens standing in for the unknown total_q
+    if (!non_overlapping(st->q_tokens, st->o_row, H, st->o_head, D))
+        return fail(ATTN_VARLEN_EINVAL, "out strides (row %lld, head %lld) make elements overlap",
+                    (long long)st->o_row, (long long)st->o_head);
+    if (lse && H > 1 && st->lse_head != 0 && st->lse_head < st->q_tokens)
+        return fail(ATTN_VARLEN_EINVAL, "lse_head %lld is smaller than q_tokens %lld", (long long)st->lse_head,
+                    (long long)st->q_tokens);
+    const int32_t bm = avf_block_m(D);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t* ws = static_cast<int32_t*>(workspace);
+    hipError_t e = avf_plan_launch(cu_q_dev, cu_k_dev, B, H, bm, 0, max_q, max_k, st->q_tokens, st->k_tokens, ws, s);
+    if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "planner launch failed: %s", hipGetErrorString(e));
+    const int64_t grid = async_grid(async_tile_bound(st->q_tokens, B, H, bm, max_q));
+    if (grid == 0) return ATTN_VARLEN_OK;
+    AvfLaunchArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q; a.k = k; a.v = v; a.o = out; a.lse = lse;
+    a.q_row = st->q_row; a.q_head = st->q_head;
+    a.k_row = st->k_row; a.k_head = st->k_head;
+    a.v_row = st->v_row; a.v_head = st->v_head;
+    a.o_row = st->o_row; a.o_head = st->o_head;
+    a.lse_head = st->lse_head ? st->lse_head : st->q_tokens;
+    a.scale = scale;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    a.num_heads = H;
+    a.causal = (flags & ATTN_VARLEN_CAUSAL) ? 1 : 0;
+    a.dev_plan = ws;
+    a.cu_q = cu_q_dev;
+    a.cu_k = cu_k_dev;
+    a.num_segs = B;
+    a.num_tiles = (int32_t)grid;
+    e = avf_launch(a, D, s);
+    if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ATTN_VARLEN_OK;
+}
+
+int32_t attn_varlen_async_status(const void* workspace, void* stream, int32_t* status) {
+    g_last_error.clear();
+    if (!workspace || !status) return fail(ATTN_VARLEN_ENULL, "workspace and status must be non-NULL");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t word = 0;
+    hipError_t e = hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "reading the workspace status failed: %s", hipGetErrorString(e));
+    *status = word;
+    return ATTN_VARLEN_OK;
+}
+
+}  // extern "C"

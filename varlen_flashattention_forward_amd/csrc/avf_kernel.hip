@@ -94,7 +94,10 @@ struct Tile {
 
 // CAUSAL (compile-time): apply the causal mask. A separate instantiation, so
 // the unmasked kernel carries none of its per-row limits or extra stage loop.
-template <int D, int QB, int NW, int BN, bool CAUSAL>
+// DEVPLAN (compile-time): the tile plan was built on the device (no host
+// read-back of cu_seqlens); the grid is a bound, every workgroup loops over
+// tiles and leaves the loop at the plan's real tile count (below).
+template <int D, int QB, int NW, int BN, bool CAUSAL, bool DEVPLAN>
 __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs a) {
     using T = Tile<D, QB, NW, BN>;
     constexpr int BM = T::BM;
@@ -108,20 +111,20 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     const int l32 = lane & 31;
     const int hf = lane >> 5;
 
-    // ---- tile decode (the grid is exact: every workgroup owns a real tile) ----
-    const int32_t linear = avf_linear_tile((int32_t)blockIdx.x, a.num_tiles);
-    const AvfTile tile = avf_decode(linear, a.tile_start, a.q_start, a.num_segs, a.num_heads, BM);
-    const int32_t seg = tile.seg;
-    const int32_t h = tile.head;
-    const int32_t lq = a.q_start[seg + 1] - a.q_start[seg];
-    const int32_t lk = a.k_start[seg + 1] - a.k_start[seg];
+    // One tile: query block tile_mblk (in dispatch order) of head h of the
+    // launch's segment seg, whose query rows are [qs0, qs1) and key rows
+    // [ks0, ks1) of the packed tensors.
+    auto run_tile = [&](const int32_t seg, const int32_t tile_mblk, const int32_t h, const int32_t qs0,
+                        const int32_t qs1, const int32_t ks0, const int32_t ks1) {
+    const int32_t lq = qs1 - qs0;
+    const int32_t lk = ks1 - ks0;
     // Causal: later query blocks see more keys, so they are dispatched first
     // (the block order within a (segment, head) is reversed).
-    const int32_t mblk = CAUSAL ? (lq + BM - 1) / BM - 1 - tile.mblk : tile.mblk;
+    const int32_t mblk = CAUSAL ? (lq + BM - 1) / BM - 1 - tile_mblk : tile_mblk;
     const int32_t row0 = mblk * BM;
     const int32_t rows_here = min(BM, lq - row0);
-    const int64_t q_tok0 = (int64_t)a.q_start[seg] + row0;
-    const int64_t k_tok0 = (int64_t)a.k_start[seg];
+    const int64_t q_tok0 = (int64_t)qs0 + row0;
+    const int64_t k_tok0 = (int64_t)ks0;
     const int64_t gseg = (int64_t)a.seg0 + seg;  // batched tensors: per-segment base offsets
     // Keys the tile needs: all of the segment, or with the causal mask (row r
     // sees keys j <= r + lk - lq) those up to its last row's limit. Keys below
@@ -540,16 +543,50 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
             }
         }
     }
+    };
+
+    if constexpr (!DEVPLAN) {
+        // the grid is exact: every workgroup owns a real tile
+        const int32_t linear = avf_linear_tile((int32_t)blockIdx.x, a.num_tiles);
+        const AvfTile tile = avf_decode(linear, a.tile_start, a.q_start, a.num_segs, a.num_heads, BM);
+        run_tile(tile.seg, tile.mblk, tile.head, a.q_start[tile.seg], a.q_start[tile.seg + 1], a.k_start[tile.seg],
+                 a.k_start[tile.seg + 1]);
+    } else {
+        // Device plan (workspace written by the planner kernel earlier on the
+        // stream): word 0 the status of its cu_seqlens check, word 1 the tile
+        // count, then the tile prefix. Invalid cu_seqlens: no workgroup forms
+        // any address. Otherwise workgroup w takes tiles w, w + G, ... below
+        // the count (G = gridDim.x, a multiple of 8, so a workgroup stays on
+        // its XCD's contiguous run of tiles).
+        const int32_t* plan = a.dev_plan;
+        if (plan[0] != 0) return;
+        const int32_t nt = plan[1];
+        for (int32_t idx = (int32_t)blockIdx.x; idx < nt; idx += (int32_t)gridDim.x) {
+            const int32_t linear = avf_linear_tile(idx, nt);
+            const AvfTile tile = avf_decode(linear, plan + AVF_PLAN_HEADER_WORDS, a.cu_q, a.num_segs, a.num_heads, BM);
+            run_tile(tile.seg, tile.mblk, tile.head, a.cu_q[tile.seg], a.cu_q[tile.seg + 1], a.cu_k[tile.seg],
+                     a.cu_k[tile.seg + 1]);
+            // the next tile's first loads overwrite LDS buffers this one read
+            __syncthreads();
+        }
+    }
 }
 
 template <int D, int QB, int NW, int BN>
 hipError_t launch_cfg(const AvfLaunchArgs& a, hipStream_t stream) {
-    if (a.causal)
-        hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true>), dim3((uint32_t)a.num_tiles), dim3(NW * 64), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false>), dim3((uint32_t)a.num_tiles), dim3(NW * 64), 0,
-                           stream, a);
+    // grid: the exact tile count, or with a device plan the host's bound
+    const dim3 grid((uint32_t)a.num_tiles), block(NW * 64);
+    if (a.dev_plan) {
+        if (a.causal)
+            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false, true>), grid, block, 0, stream, a);
+    } else {
+        if (a.causal)
+            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true, false>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false, false>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 

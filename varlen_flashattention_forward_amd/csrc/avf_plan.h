@@ -29,6 +29,12 @@ struct AvfLaunchArgs {
     int64_t q_seg, k_seg, v_seg, o_seg, lse_seg;
     int32_t seg0;       // global index of this launch's first segment
     int32_t causal;     // 1: query row r of a segment sees keys j <= r + Lk - Lq
+    // Device plan (sync-free entry): the planner's workspace (status, tile
+    // count, tile prefix of all num_segs segments) and the caller's device
+    // cu_seqlens; NULL for a host-planned launch, which uses the arrays below.
+    const int32_t* dev_plan;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
     float scale_log2e;  // softmax_scale * log2(e): logits in base-2 units
     float scale;        // softmax_scale: the LSE is reported in natural-log units
     int32_t num_heads;
@@ -40,6 +46,11 @@ struct AvfLaunchArgs {
     int32_t q_start[AVF_SEGS_PER_LAUNCH + 1];
     int32_t k_start[AVF_SEGS_PER_LAUNCH + 1];
 };
+
+// Device-plan workspace: AVF_PLAN_HEADER_WORDS int32 words (status, tile
+// count, two reserved), then tile_start[0..B] (tile_start[b] = H * sum over
+// segments b' < b of ceil(L_b' / block)).
+#define AVF_PLAN_HEADER_WORDS 4
 
 struct AvfTile {
     int32_t seg, mblk, head;
@@ -89,6 +100,13 @@ __host__ __device__ inline int64_t avf_elem_offset(int64_t row, int64_t row_stri
     return row * row_stride + head * head_stride;
 }
 
-// Host-side launcher implemented next to the kernels.
+// Host-side launchers implemented next to the kernels.
 hipError_t avf_launch(const AvfLaunchArgs& args, int32_t head_dim, hipStream_t stream);
+// Planner: validates cu_seqlens_q/k (B+1 device entries each) against the
+// bounds and writes the workspace above for blocks of `block` rows of the
+// `tiled` side (0: query rows, 1: key rows). Status: 0, or
+// ATTN_VARLEN_ECU / ATTN_VARLEN_EMAXSEQ / ATTN_VARLEN_EUNSUPPORTED.
+hipError_t avf_plan_launch(const int32_t* cu_q, const int32_t* cu_k, int32_t num_segs, int32_t num_heads,
+                           int32_t block, int32_t tiled, int32_t max_q, int32_t max_k, int64_t q_tokens,
+                           int64_t k_tokens, int32_t* workspace, hipStream_t stream);
 int32_t avf_block_m(int32_t head_dim);
