@@ -31,6 +31,14 @@ def _widen(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def _source(x):
+    """(array, widen): float64 arrays are used as they are; bf16 inputs (bits or
+    CPU tensors) are widened exactly, slice by slice."""
+    if isinstance(x, np.ndarray) and x.dtype == np.float64:
+        return x, (lambda a: a)
+    return _bits(x), _widen
+
+
 def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, rows=None,
                     row_chunk: int = 128, threads: int | None = None, causal: bool = False):
     """Returns (out [R, H, D] float64, lse [R, H] float64) for the requested
@@ -38,8 +46,9 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, rows=None
     pairs run on `threads` Python threads, each with single-threaded BLAS.
     causal: row r of a segment sees keys j <= r + Lk - Lq (bottom-right
     aligned, the same reading as the C oracle); a row that sees no key gives
-    o = 0 and lse = -inf."""
-    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    o = 0 and lse = -inf. q, k, v are bf16 (bits or CPU tensors) or float64
+    arrays (the fp8 oracle passes dequantized values)."""
+    (qb, wq), (kb, wk), (vb, wv) = _source(q), _source(k), _source(v)
     if qb.ndim != 3 or kb.ndim != 3 or kb.shape != vb.shape or kb.shape[1:] != qb.shape[1:]:
         raise ValueError("q must be [Nq,H,D] and k, v [Nk,H,D] with the same H, D")
     cq = np.asarray(cu_seqlens_q, dtype=np.int64)
@@ -61,11 +70,11 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, rows=None
         if ke == ks:
             lse[sel, h] = -np.inf
             return
-        K = _widen(kb[ks:ke, h, :])
-        V = _widen(vb[ks:ke, h, :])
+        K = wk(kb[ks:ke, h, :])
+        V = wv(vb[ks:ke, h, :])
         for c0 in range(0, sel.size, row_chunk):
             idx = sel[c0:c0 + row_chunk]
-            Q = _widen(qb[rows[idx], h, :])
+            Q = wq(qb[rows[idx], h, :])
             S = scale * (Q @ K.T)
             if causal:
                 last = rows[idx] - cq[b] + (ke - ks) - (cq[b + 1] - cq[b])  # last visible key
