@@ -32,6 +32,9 @@ sys.path.insert(0, str(ROOT))
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
+# 8-bit score product + bf16 P.V: half the FLOPs at each rate, time-weighted
+PEAK_FP8_QK_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 KERNEL_SOURCES = ["varlen_flashattention_forward_amd/csrc/avf_kernel.hip",
                   "varlen_flashattention_forward_amd/csrc/avf_plan.h",
                   "varlen_flashattention_forward_amd/csrc/avf_device.h"]
@@ -204,6 +207,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--async", dest="use_async", action="store_true",
                     help="time the sync-free entry point (device planner, no host read-back)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the low-precision forward (E4M3 q and k, 8-bit score product)")
     ap.add_argument("--backward", action="store_true", help="time the backward pass (default workload bwd_9728)")
     ap.add_argument("--cpu-rows-bwd", type=int, default=8, help="dq rows per segment for the backward CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -244,9 +249,17 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     ws = avf.async_workspace(w.num_segments, dev) if args.use_async else None
+    ws8 = None
+    if args.fp8:
+        ws8 = torch.empty(avf.fp8_workspace_bytes(w.total_q, w.total_k, w.num_heads, w.head_dim), dtype=torch.uint8,
+                          device=dev)
 
     def step():
-        if args.use_async:
+        if args.fp8:
+            avf.attn_varlen_fwd_fp8(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                                    workspace=ws8, softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"],
+                                    causal=w.causal)
+        elif args.use_async:
             avf.attn_varlen_fwd_async(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
                                       workspace=ws, softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"],
                                       causal=w.causal)
@@ -275,7 +288,12 @@ def main() -> int:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        if args.use_async:
+        if args.fp8:
+            avf.attn_varlen_fwd_fp8(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                                    workspace=ws8, softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"],
+                                    cu_seqlens_q_host=cu_q, cu_seqlens_k_host=cu_k, stream=stream.cuda_stream,
+                                    causal=w.causal)
+        elif args.use_async:
             step()  # planner + attention kernel on the current stream
         else:
             avf.attn_varlen_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
@@ -292,8 +310,11 @@ def main() -> int:
     achieved = flops / launches / (kms / launches / 1e3) / 1e12
     log(f"[bench] kernel: {kms:.3f} ms/call over {launches} launch(es), {wgs} workgroups, {achieved:.1f} TFLOP/s")
     traffic = traffic_for(w.name)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+    peak = PEAK_FP8_QK_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
+    if args.fp8:
+        traffic = None  # the counters were taken on the bf16 kernel
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel_ms": round(kms / launches, 4), "algorithmic_flops_per_launch": flops // launches,
                 "algorithmic_bytes_per_launch": w.algorithmic_bytes() // launches}
 
@@ -304,7 +325,8 @@ def main() -> int:
         log(f"[bench] cpu baseline {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
 
     rec = {
-        "metric": "attention fwd TFLOP/s (4*Sq*Sk*D*H) and % of MI355X bf16 MFMA peak",
+        "metric": ("attention fwd TFLOP/s (4*Sq*Sk*D*H), 8-bit q.k, and % of the MI355X fp8/bf16 MFMA peak mix"
+                   if args.fp8 else "attention fwd TFLOP/s (4*Sq*Sk*D*H) and % of MI355X bf16 MFMA peak"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -314,15 +336,16 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8e4m3 q.k, bf16 p.v" if args.fp8 else "bf16",
         "data": "synthetic",
-        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "pct_of_peak": round(100.0 * value / peak, 2),
         "config": {"workload": w.name, "num_heads": w.num_heads, "head_dim": w.head_dim,
                    "segments": w.num_segments, "total_q": w.total_q, "total_k": w.total_k,
                    "max_seqlen_q": w.max_seqlen_q, "max_seqlen_k": w.max_seqlen_k,
                    "layout": w.layout, "causal": w.causal, "flops_per_step": flops,
                    "workgroups": wgs, "block_m": avf.block_m(w.head_dim),
-                   "entry": "attn_varlen_fwd_async" if args.use_async else "attn_varlen_fwd"},
+                   "entry": ("attn_varlen_fwd_fp8" if args.fp8 else
+                             "attn_varlen_fwd_async" if args.use_async else "attn_varlen_fwd")},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

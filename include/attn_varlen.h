@@ -302,6 +302,50 @@ int32_t attn_varlen_async_grid(int64_t q_tokens, int32_t num_segments, int32_t n
                                int32_t head_dim, int32_t max_seqlen_q, int64_t* workgroups);
 
 /*
+ * ---- Low-precision forward (8-bit score product) ---------------------------
+ *
+ * The CDNA4 counterpart of the quantized forward of the "ffpa-attn PR #387"
+ * page (its NVFP4 path; "Verification": cos ~0.982 against SDPA, the
+ * quantization error), with every size that scales with the sequence length
+ * in 64-bit arithmetic (that page's "Fix"). Steps, all on `stream`:
+ *   1. per head h: amax_q[h] = max |q[i,h,d]| over rows [0, cu_q[B]), amax_k
+ *      likewise over [0, cu_k[B]);
+ *   2. codes = E4M3(x * (448 / amax)) (fp32 product, round to nearest even,
+ *      OCP E4M3FN), packed [rows, H, D] in the workspace;
+ *   3. the forward with S = (codes_q . codes_k) * amax_q/448 * amax_k/448 on
+ *      the depth-64 8-bit MFMA; softmax, P (bf16) and P.V (bf16 V) as in
+ *      attn_varlen_fwd. Outputs have the same meaning and layout.
+ * head_dim 64 or 128 (else ATTN_VARLEN_EUNSUPPORTED); other arguments and
+ * errors as attn_varlen_fwd_ex / attn_varlen_fwd_hostcu_ex, plus
+ *   workspace        caller-owned device buffer of
+ *                    attn_varlen_fp8_workspace_bytes(cu_q[B], cu_k[B], H, D)
+ *                    bytes, 256-byte aligned: amax words (2*H uint32, fp32
+ *                    bits: q heads, then k heads) at offset 0, then the q and
+ *                    k codes at the offsets attn_varlen_fp8_workspace_offsets
+ *                    reports. Overwritten by every call.
+ */
+int64_t attn_varlen_fp8_workspace_bytes(int64_t total_q, int64_t total_k, int32_t num_heads,
+                                        int32_t head_dim);
+int32_t attn_varlen_fp8_workspace_offsets(int64_t total_q, int64_t total_k, int32_t num_heads,
+                                          int32_t head_dim, int64_t* q8_offset, int64_t* k8_offset);
+
+int32_t attn_varlen_fwd_fp8(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int32_t num_segments, int32_t num_heads, int32_t head_dim,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            const attn_varlen_layout* layout, float softmax_scale, uint32_t flags,
+                            void* workspace, int64_t workspace_bytes, void* out, float* lse,
+                            void* stream);
+
+int32_t attn_varlen_fwd_fp8_hostcu(const void* q, const void* k, const void* v,
+                                   const int32_t* cu_seqlens_q_host,
+                                   const int32_t* cu_seqlens_k_host, int32_t num_segments,
+                                   int32_t num_heads, int32_t head_dim, int32_t max_seqlen_q,
+                                   int32_t max_seqlen_k, const attn_varlen_layout* layout,
+                                   float softmax_scale, uint32_t flags, void* workspace,
+                                   int64_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
  * ---- Backward -------------------------------------------------------------
  *
  * Gradients of the varlen forward above for an upstream gradient

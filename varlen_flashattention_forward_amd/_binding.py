@@ -28,7 +28,8 @@ EXPORTED_SYMBOLS = (
     "attn_fwd_batched", "attn_fwd_batched_validate",
     "attn_varlen_bwd_preprocess", "attn_varlen_bwd", "attn_varlen_bwd_hostcu", "attn_varlen_bwd_validate",
     "attn_varlen_bwd_grid_plan", "attn_varlen_async_workspace_bytes", "attn_varlen_fwd_async",
-    "attn_varlen_async_status", "attn_varlen_async_grid",
+    "attn_varlen_async_status", "attn_varlen_async_grid", "attn_varlen_fp8_workspace_bytes",
+    "attn_varlen_fp8_workspace_offsets", "attn_varlen_fwd_fp8", "attn_varlen_fwd_fp8_hostcu",
 )
 
 CAUSAL = 1  # ATTN_VARLEN_CAUSAL
@@ -117,6 +118,15 @@ def lib():
         L.attn_varlen_async_status.argtypes = [_vp, _vp, _i32p]
         L.attn_varlen_async_grid.restype = ctypes.c_int32
         L.attn_varlen_async_grid.argtypes = [ctypes.c_int64] + [ctypes.c_int32] * 4 + [_i64p]
+        L.attn_varlen_fp8_workspace_bytes.restype = ctypes.c_int64
+        L.attn_varlen_fp8_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+        L.attn_varlen_fp8_workspace_offsets.restype = ctypes.c_int32
+        L.attn_varlen_fp8_workspace_offsets.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                                        ctypes.c_int32, _i64p, _i64p]
+        for name in ("attn_varlen_fwd_fp8", "attn_varlen_fwd_fp8_hostcu"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int32
+            f.argtypes = fwd_args[:12] + [ctypes.c_uint32, _vp, ctypes.c_int64] + fwd_args[12:]
         L.attn_varlen_block_m.restype = ctypes.c_int32
         L.attn_varlen_block_m.argtypes = [ctypes.c_int32]
         L.attn_varlen_count_tiles.restype = ctypes.c_int64
@@ -361,6 +371,77 @@ def attn_varlen_fwd_async(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int
                                      ctypes.byref(layout), float(softmax_scale), CAUSAL if causal else 0,
                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                      out.data_ptr(), lse.data_ptr() if lse is not None else None, stream)
+    _check(rc)
+    return out, lse, workspace
+
+
+def fp8_workspace_bytes(total_q: int, total_k: int, num_heads: int, head_dim: int) -> int:
+    r = lib().attn_varlen_fp8_workspace_bytes(total_q, total_k, num_heads, head_dim)
+    if r < 0:
+        _check(int(r))
+    return int(r)
+
+
+def fp8_workspace_offsets(total_q: int, total_k: int, num_heads: int, head_dim: int):
+    """(q8 offset, k8 offset) in bytes; the 2*H amax words sit at offset 0."""
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().attn_varlen_fp8_workspace_offsets(total_q, total_k, num_heads, head_dim, ctypes.byref(a),
+                                                   ctypes.byref(b)))
+    return a.value, b.value
+
+
+def attn_varlen_fwd_fp8(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                        workspace=None, softmax_scale: float | None = None, out=None, lse=None,
+                        return_lse: bool = True, cu_seqlens_q_host=None, cu_seqlens_k_host=None, stream=None,
+                        causal: bool = False):
+    """Forward with per-head E4M3 q and k and the 8-bit score product
+    (head_dim 64 or 128). Same tensors as attn_varlen_fwd; `workspace` (uint8
+    device tensor of fp8_workspace_bytes) is allocated when not given.
+    Returns (out, lse, workspace)."""
+    import torch
+
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
+    total_q, H, D = q.shape
+    if k.shape[1:] != (H, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [total_k, H, D] matching q's H and D")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((total_q, H, D), dtype=torch.bfloat16, device=q.device)
+    lse_head = 0
+    if lse is None and return_lse:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        if lse.dtype != torch.float32 or lse.dim() != 2 or lse.shape[0] != H or lse.stride(1) != 1 \
+                or lse.shape[1] < total_q:
+            raise ValueError("lse must be fp32 [H, >= total_q] with unit inner stride")
+        lse_head = lse.stride(0)
+    if workspace is None:
+        workspace = torch.empty(fp8_workspace_bytes(total_q, k.shape[0], H, D), dtype=torch.uint8, device=q.device)
+    layout = _layout_of(q, k, v, out, lse, lse_head)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    tail = (ctypes.byref(layout), float(softmax_scale), CAUSAL if causal else 0, workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None, stream)
+    L = lib()
+    if cu_seqlens_q_host is not None or cu_seqlens_k_host is not None:
+        cq, B = _cu_array(cu_seqlens_q_host)
+        ck, Bk = _cu_array(cu_seqlens_k_host)
+        if B != Bk:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+        rc = L.attn_varlen_fwd_fp8_hostcu(q.data_ptr(), k.data_ptr(), v.data_ptr(), cq, ck, B, H, D,
+                                          int(max_seqlen_q), int(max_seqlen_k), *tail)
+    else:
+        for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+            if cu.dtype != torch.int32 or not cu.is_cuda or cu.dim() != 1 or not cu.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous int32 device tensor")
+        B = cu_seqlens_q.numel() - 1
+        if cu_seqlens_k.numel() != B + 1:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+        rc = L.attn_varlen_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
+                                   cu_seqlens_k.data_ptr(), B, H, D, int(max_seqlen_q), int(max_seqlen_k), *tail)
     _check(rc)
     return out, lse, workspace
 

@@ -20,7 +20,7 @@ CSRC = PKG / "csrc"
 ROOT = PKG.parent
 LIB = Path(os.environ.get("AVF_LIB_OUT", PKG / "libattn_varlen.so"))
 BUILD_DIR = Path(os.environ.get("AVF_BUILD_DIR", PKG / "_build"))
-SOURCES = ["avf_api.hip", "avf_kernel.hip", "avf_bwd_kernel.hip", "avf_planner.hip"]
+SOURCES = ["avf_api.hip", "avf_kernel.hip", "avf_bwd_kernel.hip", "avf_planner.hip", "avf_quant.hip"]
 ARCH = os.environ.get("AVF_OFFLOAD_ARCH", "gfx950")
 
 

@@ -16,6 +16,7 @@
 #include "../../include/attn_varlen.h"
 #include "avf_bwd_plan.h"
 #include "avf_plan.h"
+#include "avf_quant.h"
 
 namespace {
 
@@ -186,9 +187,11 @@ int64_t fill_plan(AvfLaunchArgs& a, const int32_t* cu_q, const int32_t* cu_k, in
 // below 2^32 (HSA dispatch limit) with 256 threads per workgroup.
 constexpr int64_t kMaxTilesPerLaunch = (int64_t)1 << 23;
 
+// q8/k8/amax8: the 8-bit score operands (NULL for the bf16 path)
 int32_t run(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
             int32_t B, int32_t H, int32_t D, const attn_varlen_layout* st, float scale, void* out,
-            float* lse, hipStream_t stream, uint32_t flags, const SegStrides& seg) {
+            float* lse, hipStream_t stream, uint32_t flags, const SegStrides& seg,
+            const uint8_t* q8 = nullptr, const uint8_t* k8 = nullptr, const uint32_t* amax8 = nullptr) {
     const int32_t bm = avf_block_m(D);
     AvfLaunchArgs a;
     std::memset(&a, 0, sizeof a);
@@ -203,6 +206,7 @@ int32_t run(const void* q, const void* k, const void* v, const int32_t* cu_q, co
     a.num_heads = H;
     a.causal = (flags & ATTN_VARLEN_CAUSAL) ? 1 : 0;
     a.q_seg = seg.q; a.k_seg = seg.k; a.v_seg = seg.v; a.o_seg = seg.o; a.lse_seg = seg.lse;
+    a.q8 = q8; a.k8 = k8; a.amax8 = amax8;
     for (int32_t b0 = 0; b0 < B;) {
         // segments of this launch: at most AVF_SEGS_PER_LAUNCH and at most kMaxTilesPerLaunch tiles
         int32_t b1 = b0;
@@ -844,6 +848,122 @@ int32_t attn_varlen_async_status(const void* workspace, void* stream, int32_t* s
     if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "reading the workspace status failed: %s", hipGetErrorString(e));
     *status = word;
     return ATTN_VARLEN_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Low-precision forward: per-head E4M3 Q and K, 8-bit score product
+
+namespace {
+
+struct Fp8Layout {
+    int64_t q8, k8, bytes;  // byte offsets in the workspace (amax words at 0)
+};
+
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+Fp8Layout fp8_layout(int64_t total_q, int64_t total_k, int32_t H, int32_t D) {
+    Fp8Layout l;
+    l.q8 = round256(8 * (int64_t)H);
+    l.k8 = l.q8 + round256(total_q * H * D);
+    l.bytes = l.k8 + round256(total_k * H * D);
+    return l;
+}
+
+bool fp8_dim(int32_t D) { return D == 64 || D == 128; }
+
+int32_t fp8_run(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k, int32_t B,
+                int32_t H, int32_t D, const attn_varlen_layout* st, float scale, uint32_t flags, void* workspace,
+                int64_t workspace_bytes, void* out, float* lse, hipStream_t s) {
+    const Fp8Layout l = fp8_layout(cu_q[B], cu_k[B], H, D);
+    if (workspace_bytes < l.bytes)
+        return fail(ATTN_VARLEN_EINVAL, "workspace of %lld bytes is smaller than the %lld needed",
+                    (long long)workspace_bytes, (long long)l.bytes);
+    char* ws = static_cast<char*>(workspace);
+    AvfQuantArgs qa;
+    qa.q = q; qa.k = k;
+    qa.q_rows = cu_q[B]; qa.k_rows = cu_k[B];
+    qa.q_row = st->q_row; qa.q_head = st->q_head; qa.k_row = st->k_row; qa.k_head = st->k_head;
+    qa.num_heads = H; qa.head_dim = D;
+    qa.amax = reinterpret_cast<uint32_t*>(ws);
+    qa.q8 = reinterpret_cast<uint8_t*>(ws + l.q8);
+    qa.k8 = reinterpret_cast<uint8_t*>(ws + l.k8);
+    const hipError_t e = avf_fp8_quantize(qa, s);
+    if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "quantization launch failed: %s", hipGetErrorString(e));
+    return run(q, k, v, cu_q, cu_k, B, H, D, st, scale, out, lse, s, flags, SegStrides{0, 0, 0, 0, 0}, qa.q8, qa.k8,
+               qa.amax);
+}
+
+int32_t fp8_check(int32_t D, const void* workspace) {
+    if (!fp8_dim(D)) return fail(ATTN_VARLEN_EUNSUPPORTED, "head_dim %d not supported by the 8-bit path (64 or 128)", D);
+    if (!workspace) return fail(ATTN_VARLEN_ENULL, "workspace must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(ATTN_VARLEN_EALIGN, "workspace must be 256-byte aligned");
+    return ATTN_VARLEN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t attn_varlen_fp8_workspace_bytes(int64_t total_q, int64_t total_k, int32_t H, int32_t D) {
+    g_last_error.clear();
+    if (total_q < 0 || total_k < 0 || H <= 0) return fail(ATTN_VARLEN_EINVAL, "bad sizes");
+    if (!fp8_dim(D)) return fail(ATTN_VARLEN_EUNSUPPORTED, "head_dim %d not supported by the 8-bit path", D);
+    return fp8_layout(total_q, total_k, H, D).bytes;
+}
+
+int32_t attn_varlen_fp8_workspace_offsets(int64_t total_q, int64_t total_k, int32_t H, int32_t D, int64_t* q8_offset,
+                                          int64_t* k8_offset) {
+    g_last_error.clear();
+    if (!q8_offset || !k8_offset) return fail(ATTN_VARLEN_ENULL, "NULL argument");
+    const int64_t b = attn_varlen_fp8_workspace_bytes(total_q, total_k, H, D);
+    if (b < 0) return (int32_t)b;
+    const Fp8Layout l = fp8_layout(total_q, total_k, H, D);
+    *q8_offset = l.q8;
+    *k8_offset = l.k8;
+    return ATTN_VARLEN_OK;
+}
+
+int32_t attn_varlen_fwd_fp8_hostcu(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
+                                   int32_t B, int32_t H, int32_t D, int32_t max_q, int32_t max_k,
+                                   const attn_varlen_layout* st, float scale, uint32_t flags, void* workspace,
+                                   int64_t workspace_bytes, void* out, float* lse, void* stream) {
+    g_last_error.clear();
+    int32_t rc = check_flags(flags);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    rc = validate_all(q, k, v, cu_q, cu_k, B, H, D, max_q, max_k, st, scale, out, lse);
+    if (rc != ATTN_VARLEN_OK || B == 0) return rc;
+    if ((rc = fp8_check(D, workspace)) != ATTN_VARLEN_OK) return rc;
+    return fp8_run(q, k, v, cu_q, cu_k, B, H, D, st, scale, flags, workspace, workspace_bytes, out, lse,
+                   static_cast<hipStream_t>(stream));
+}
+
+int32_t attn_varlen_fwd_fp8(const void* q, const void* k, const void* v, const int32_t* cu_q_dev, const int32_t* cu_k_dev,
+                            int32_t B, int32_t H, int32_t D, int32_t max_q, int32_t max_k, const attn_varlen_layout* st,
+                            float scale, uint32_t flags, void* workspace, int64_t workspace_bytes, void* out, float* lse,
+                            void* stream) {
+    g_last_error.clear();
+    int32_t rc = check_flags(flags);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    rc = check_scalars(q, k, v, B, H, D, max_q, max_k, st, scale, out, lse);
+    if (rc != ATTN_VARLEN_OK || B == 0) return rc;
+    if ((rc = fp8_check(D, workspace)) != ATTN_VARLEN_OK) return rc;
+    if (!cu_q_dev || !cu_k_dev) return fail(ATTN_VARLEN_ENULL, "cu_seqlens_q/k must be non-NULL");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    std::vector<int32_t> cu((size_t)2 * (B + 1));
+    hipError_t e = hipMemcpyAsync(cu.data(), cu_q_dev, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(cu.data() + B + 1, cu_k_dev, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "reading cu_seqlens failed: %s", hipGetErrorString(e));
+    const int32_t* cq = cu.data();
+    const int32_t* ck = cu.data() + B + 1;
+    rc = check_cu(cq, ck, B, max_q, max_k, st);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    rc = check_with_cu(cq, B, H, D, st, lse);
+    if (rc != ATTN_VARLEN_OK) return rc;
+    return fp8_run(q, k, v, cq, ck, B, H, D, st, scale, flags, workspace, workspace_bytes, out, lse, s);
 }
 
 }  // extern "C"

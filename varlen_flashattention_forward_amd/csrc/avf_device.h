@@ -16,6 +16,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // gfx9 raw buffer descriptor word 3: 32-bit data format, no swizzle, no
 // index stride; records are bytes and out-of-range loads return 0.

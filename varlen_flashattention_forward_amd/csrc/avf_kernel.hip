@@ -68,11 +68,18 @@ template <int D>
 __device__ constexpr int v_swz(int key) {
     return D == 128 ? (key & 3) << 2 : D == 64 ? ((key >> 1) & 1) << 2 : 0;
 }
+// 8-bit K rows (D bytes; ds_read_b128, 16 consecutive keys per phase):
+//   D = 128 (8 chunks, two rows per 256 bytes): chunk ^= (key / 2) % 8;
+//   D = 64 (4 chunks, four rows per 256 bytes): chunk ^= (key / 4) % 4.
+template <int D>
+__device__ constexpr int k8_swz(int key) {
+    return D == 128 ? (key >> 1) & 7 : (key >> 2) & 3;
+}
 
 // LDS holds a ring of KBUF K stages followed by a ring of VBUF V stages. V
 // lives one stage longer than K because each wave's P.V product trails its
 // Q.K^T product by one 32-key sub-block, across stage boundaries.
-template <int D, int QB, int NW, int BN>
+template <int D, int QB, int NW, int BN, bool F8 = false>
 struct Tile {
     static constexpr int NT = NW * 64;          // threads per workgroup
     static constexpr int BM = QB * 32 * NW;     // query rows per tile
@@ -82,7 +89,12 @@ struct Tile {
     static constexpr int ROWB = D * 2;          // bytes per K/V row in LDS
     static constexpr int SBYTES = BN * ROWB;    // one stage of K (or of V)
     static constexpr int KBUF = 2, VBUF = 3;
-    static constexpr int LDS_BYTES = (KBUF + VBUF) * SBYTES;
+    // K stages hold bf16 rows, or with F8 the E4M3 codes (D bytes per row)
+    static constexpr int KROWB = F8 ? D : 2 * D;
+    static constexpr int KSBYTES = BN * KROWB;
+    static constexpr int KQ = D / 64;           // F8: depth-64 Q.K^T MFMAs per sub-block
+    static constexpr int NIK = KSBYTES / 1024;  // 1 KiB direct loads per K stage
+    static constexpr int LDS_BYTES = KBUF * KSBYTES + VBUF * SBYTES;
     static constexpr int NI = SBYTES / 1024;    // 1 KiB direct loads per array and stage
     static constexpr int NIW = NI / NW;         // ... per wave
     static constexpr int LPS = 2 * NIW;         // direct loads per wave and stage (K and V)
@@ -90,6 +102,7 @@ struct Tile {
     static_assert(KB >= 4 && KB % 2 == 0, "four or more sub-blocks per stage, parity repeating every stage");
     static_assert(NI % NW == 0, "every wave issues the same number of loads per stage");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS rings");
+    static_assert(!F8 || (D % 64 == 0 && NIK % NW == 0), "8-bit K stages: depth-64 steps, whole loads per wave");
 };
 
 // CAUSAL (compile-time): apply the causal mask. A separate instantiation, so
@@ -97,9 +110,11 @@ struct Tile {
 // DEVPLAN (compile-time): the tile plan was built on the device (no host
 // read-back of cu_seqlens); the grid is a bound, every workgroup loops over
 // tiles and leaves the loop at the plan's real tile count (below).
-template <int D, int QB, int NW, int BN, bool CAUSAL, bool DEVPLAN>
+// F8 (compile-time): S^T = K Q^T from per-head E4M3 codes of q and k with the
+// depth-64 8-bit MFMA (v_mfma_f32_32x32x64_f8f6f4); P.V stays bf16.
+template <int D, int QB, int NW, int BN, bool CAUSAL, bool DEVPLAN, bool F8>
 __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs a) {
-    using T = Tile<D, QB, NW, BN>;
+    using T = Tile<D, QB, NW, BN, F8>;
     constexpr int BM = T::BM;
     __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
     // LDS byte address of the array (M0 operand of the direct loads)
@@ -139,14 +154,30 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     const char* qptr = (const char*)a.q + 2 * (avf_elem_offset(q_tok0, a.q_row, h, a.q_head) + gseg * a.q_seg);
     const auto qrs = make_rsrc(qptr, (uint32_t)(rows_here - 1) * q_rs + 2 * D);
     const int wrow0 = wave * QB * 32;
-    bf16x8 qf[QB][T::KS];
+    bf16x8 qf[QB][F8 ? 1 : T::KS];
+    i32x8 qf8[QB][F8 ? T::KQ : 1];  // F8: lane holds dims 64t + 32*hf .. +32 of its row
+    if constexpr (F8) {
+        const uint32_t q8_rs = (uint32_t)(a.num_heads * D);
+        const uint8_t* q8p = a.q8 + (q_tok0 * a.num_heads + h) * D;
+        const auto q8rs = make_rsrc(q8p, (uint32_t)(rows_here - 1) * q8_rs + D);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) {
-            const uint32_t off = (uint32_t)(wrow0 + qb * 32 + l32) * q_rs + (ks * 16 + hf * 8) * 2;
-            qf[qb][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
-        }
+            for (int t = 0; t < T::KQ; ++t) {
+                const uint32_t off = (uint32_t)(wrow0 + qb * 32 + l32) * q8_rs + 64 * t + 32 * hf;
+                const i32x4 lo = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(q8rs, off, 0, 0));
+                const i32x4 hi = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(q8rs, off + 16, 0, 0));
+                qf8[qb][t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+    } else {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int ks = 0; ks < T::KS; ++ks) {
+                const uint32_t off = (uint32_t)(wrow0 + qb * 32 + l32) * q_rs + (ks * 16 + hf * 8) * 2;
+                qf[qb][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
+            }
+    }
 
     f32x16 o[QB][T::DB];
 #pragma unroll
@@ -165,7 +196,16 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
         mc_i[qb] = -INFINITY;
         l_i[qb] = 0.f;
     }
-    const float c = a.scale_log2e;  // weights are exp2(c * (s - m))
+    float c = a.scale_log2e;  // weights are exp2(c * (s - m))
+    float lse_scale = a.scale;
+    if constexpr (F8) {
+        // s is the product of codes: true scores are s * (amax_q/448) * (amax_k/448)
+        const float aq = __uint_as_float(a.amax8[h]);
+        const float ak = __uint_as_float(a.amax8[a.num_heads + h]);
+        const float sqk = (aq > 0.f ? aq / 448.f : 1.f) * (ak > 0.f ? ak / 448.f : 1.f);
+        c *= sqk;
+        lse_scale *= sqk;
+    }
 
     // ---- K/V staging: buffer loads straight into LDS ----
     // Stage j covers keys [j*BN, j*BN + BN) of the segment. Each wave issues
@@ -182,10 +222,34 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
         const int32_t nk = min(BN, k_end - key0);
         const char* kp = (const char*)a.k + 2 * (avf_elem_offset(k_tok0 + key0, a.k_row, h, a.k_head) + gseg * a.k_seg);
         const char* vp = (const char*)a.v + 2 * (avf_elem_offset(k_tok0 + key0, a.v_row, h, a.v_head) + gseg * a.v_seg);
-        const i32x4 krs = rsrc_words(kp, (uint32_t)(nk - 1) * k_rs + 2 * D);
         const i32x4 vrs = rsrc_words(vp, (uint32_t)(nk - 1) * v_rs + 2 * D);
-        const uint32_t kl = lds_addr + kbuf * T::SBYTES;
-        const uint32_t vl = lds_addr + (T::KBUF + vbuf) * T::SBYTES;
+        const uint32_t kl = lds_addr + kbuf * T::KSBYTES;
+        const uint32_t vl = lds_addr + T::KBUF * T::KSBYTES + vbuf * T::SBYTES;
+        if constexpr (F8) {
+            const uint32_t k8_rs = (uint32_t)(a.num_heads * D);
+            const uint8_t* k8p = a.k8 + ((k_tok0 + key0) * a.num_heads + h) * D;
+            const i32x4 k8rs = rsrc_words(k8p, (uint32_t)(nk - 1) * k8_rs + D);
+#pragma unroll
+            for (int m = 0; m < T::NIK / NW; ++m) {
+                const int i = wave + NW * m;
+                const int pos = i * 1024 + 16 * lane;
+                const int key = pos / T::KROWB;
+                const int slot = (pos % T::KROWB) >> 4;
+                const uint32_t kc = (uint32_t)min(key, nk - 1);
+                load_lds16(k8rs, kl + i * 1024, kc * k8_rs + ((slot ^ k8_swz<D>(key)) << 4));
+            }
+#pragma unroll
+            for (int m = 0; m < T::NIW; ++m) {
+                const int i = wave + NW * m;
+                const int pos = i * 1024 + 16 * lane;
+                const int key = pos / T::ROWB;
+                const int slot = (pos % T::ROWB) >> 4;
+                const uint32_t kc = (uint32_t)min(key, nk - 1);
+                load_lds16(vrs, vl + i * 1024, kc * v_rs + ((slot ^ v_swz<D>(key)) << 4));
+            }
+            return;
+        }
+        const i32x4 krs = rsrc_words(kp, (uint32_t)(nk - 1) * k_rs + 2 * D);
 #pragma unroll
         for (int m = 0; m < T::NIW; ++m) {
             const int i = wave + NW * m;
@@ -206,10 +270,19 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     // per-lane byte offsets are fixed; kcur holds them for the K buffer being
     // read now and moves to the other buffer once per stage, so every
     // fragment read is one LDS instruction with an immediate sub-block offset.
-    constexpr int SUB = 32 * T::ROWB;  // bytes per 32-key sub-block
-    int kcur[T::KS];
+    constexpr int SUB = 32 * T::ROWB;    // bytes per 32-key sub-block of V (and of bf16 K)
+    constexpr int SUBK = 32 * T::KROWB;  // ... of K
+    // F8: depth-64 fragment t of the lane is chunks 4t + 2*hf and 4t + 2*hf + 1
+    // of its key's row (kcur[2t], kcur[2t + 1])
+    constexpr int NKC = F8 ? 2 * T::KQ : T::KS;
+    int kcur[NKC];
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) kcur[ks] = l32 * T::ROWB + (((2 * ks + hf) ^ k_swz<D>(l32)) << 4);
+    for (int u = 0; u < NKC; ++u) {
+        if constexpr (F8)
+            kcur[u] = l32 * T::KROWB + (((4 * (u >> 1) + 2 * hf + (u & 1)) ^ k8_swz<D>(l32)) << 4);
+        else
+            kcur[u] = l32 * T::ROWB + (((2 * u + hf) ^ k_swz<D>(l32)) << 4);
+    }
     // V^T fragment for keys [kb*32 + 16*k2, +16) and dims [db*32, +32): two
     // transposing 8-byte reads. In each 16-lane group, lane j receives element
     // j%4 of the 8-byte rows read by lanes 4t + j/4 (t = 0..3); reading key
@@ -225,7 +298,7 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
 #pragma unroll
     for (int db = 0; db < T::DB; ++db) {
         const int d = db * 32 + vdim;
-        vcur[db] = T::KBUF * T::SBYTES + vkey * T::ROWB + (((d >> 3) ^ v_swz<D>(vkey)) << 4) + (d & 4) * 2;
+        vcur[db] = T::KBUF * T::KSBYTES + vkey * T::ROWB + (((d >> 3) ^ v_swz<D>(vkey)) << 4) + (d & 4) * 2;
     }
     // S^T for 32 keys x (QB*32) query rows
     auto qk = [&](const bf16x8 (&ka)[T::KS], f32x16 (&sc)[QB]) {
@@ -340,10 +413,21 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     // stage j+2 is loaded into exactly those two buffers.
     f32x16 sc[2][QB];      // scores of sub-blocks with even / odd index
     bf16x8 pk[2][QB][2];   // their weights as bf16 P^T operands
-    bf16x8 fr[T::KS];      // rotating K / V^T fragment registers
+    bf16x8 fr[F8 ? 1 : T::KS];      // rotating K / V^T fragment registers
+    i32x8 kf8[F8 ? T::KQ : 1];      // F8: K fragments (refilled one iteration ahead)
+    bf16x8 vfr[F8 ? T::KS : 1];     // F8: V^T fragments (refilled one iteration ahead)
     // K fragment u of sub-block `sub` of the K buffer being read
     auto read_k = [&](int sub, int u) {
         return *reinterpret_cast<const bf16x8*>(lds + kcur[u] + sub * SUB);
+    };
+    // F8: depth-64 K fragment t of sub-block `sub`
+    auto read_k8 = [&](int sub, int t) {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(lds + kcur[2 * t] + sub * SUBK);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(lds + kcur[2 * t + 1] + sub * SUBK);
+        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto mfma8 = [](const i32x8& ka, const i32x8& qa, const f32x16& acc) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa, acc, 0, 0, 0, 0, 0, 0);
     };
     // V^T fragment u = k2 * DB + db of sub-block `sub` of the V buffer being read
     auto read_v = [&](int sub, int u) {
@@ -411,6 +495,62 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
         for (int qb = 0; qb < QB; ++qb) psum[qb] = acc[qb][0] + acc[qb][1];
     };
 
+    // F8 iteration g: KQ slots of 8-bit Q.K^T(g+1) (each refills its K
+    // fragment with sub-block g+2), then KS slots of bf16 P.V(g-1) (each
+    // refills its V^T fragment with sub-block g, which iteration g+1
+    // multiplies); the softmax of sub-block g spreads over all KQ + KS slots
+    // as in `iterate`. vsub: sub-block g in the current V buffer.
+    auto iterate8 = [&](const f32x16 (&sv)[QB], f32x16 (&snext)[QB], bool do_qk, const bf16x8 (&pprev)[QB][2],
+                        bf16x8 (&pcur)[QB][2], float (&psum)[QB], int vsub, int ksub, bool refill_k) {
+        constexpr int NSLOT = T::KQ + T::KS;
+        float x[QB][16], pw[QB][16], acc[QB][2];
+#pragma unroll
+        for (int t = 0; t < NSLOT + 2; ++t) {
+            if (t < T::KQ) {
+                if (do_qk) {
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        const f32x16 zero = {};
+                        snext[qb] = mfma8(kf8[t], qf8[qb][t], t == 0 ? zero : snext[qb]);
+                    }
+                }
+                if (refill_k) kf8[t] = read_k8(ksub, t);
+            } else if (t < NSLOT) {
+                const int u = t - T::KQ, k2 = u / T::DB, db = u % T::DB;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[u], pprev[qb][k2], o[qb][db], 0, 0, 0);
+                vfr[u] = read_v(vsub, u);
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int te = e * NSLOT / 16;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    if (t == te) {
+                        x[qb][e] = __builtin_fmaf(sv[qb][e], c, -mc_i[qb]);
+                        pin(x[qb][e]);
+                    } else if (t == te + 1) {
+                        pw[qb][e] = __builtin_amdgcn_exp2f(x[qb][e]);
+                        pin(pw[qb][e]);
+                    } else if (t == te + 2) {
+                        acc[qb][e & 1] = e < 2 ? pw[qb][e] : acc[qb][e & 1] + pw[qb][e];
+                        pin(acc[qb][e & 1]);
+                        if (e & 1) {
+                            bf16x2 w = {(__bf16)pw[qb][e - 1], (__bf16)pw[qb][e]};
+                            pin(w);
+                            pcur[qb][e >> 3][(e & 7) - 1] = w[0];
+                            pcur[qb][e >> 3][e & 7] = w[1];
+                        }
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) psum[qb] = acc[qb][0] + acc[qb][1];
+    };
+
     // `last` (compile-time) marks the segment's final stage: keys past the
     // segment end are masked and there is no next stage. vnext is the V
     // buffer stage j+2 is loaded into. At the barrier the K reads move on to
@@ -437,31 +577,47 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
                 __syncthreads();
                 if (j + 2 < nkt) load_stage(j + 2, kbuf, vnext);
 #pragma unroll
-                for (int u = 0; u < T::KS; ++u) kcur[u] += kdelta;
+                for (int u = 0; u < NKC; ++u) kcur[u] += kdelta;
             }
-            if (kb == 1) {
+            // V reads move to stage j's buffer where they first read it: at
+            // sub-block 1 (P.V(g-1) reads V of sub-block g-1), with F8 at
+            // sub-block 0 (fragments of sub-block g are read ahead)
+            if (kb == (F8 ? 0 : 1)) {
 #pragma unroll
                 for (int db = 0; db < T::DB; ++db) vcur[db] += vdelta;
             }
             if (MASKED) mask(kb, lim, sc[kb & 1]);
             float psum[QB];
             // sub-block g-1 has the other parity
-            iterate(sc[kb & 1], sc[(kb + 1) & 1], !(LAST && kb == T::KB - 1), pk[(kb + 1) & 1], pk[kb & 1], psum,
-                    kb > 0 ? kb - 1 : T::KB - 1, (kb + 2) % T::KB, kb + 2 < T::KB || !LAST);
+            if constexpr (F8)
+                iterate8(sc[kb & 1], sc[(kb + 1) & 1], !(LAST && kb == T::KB - 1), pk[(kb + 1) & 1], pk[kb & 1], psum,
+                         kb, (kb + 2) % T::KB, kb + 2 < T::KB || !LAST);
+            else
+                iterate(sc[kb & 1], sc[(kb + 1) & 1], !(LAST && kb == T::KB - 1), pk[(kb + 1) & 1], pk[kb & 1], psum,
+                        kb > 0 ? kb - 1 : T::KB - 1, (kb + 2) % T::KB, kb + 2 < T::KB || !LAST);
             if (over_limit(psum)) fix_reference(sc[kb & 1], pk[kb & 1], psum);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) l_i[qb] += psum[qb];
         }
         if (LAST) {
-            // P.V of the segment's final sub-block
+            // P.V of the segment's final sub-block (F8: its V^T fragments are in vfr)
+            if constexpr (F8) {
 #pragma unroll
-            for (int u = 0; u < T::KS; ++u) fr[u] = read_v(T::KB - 1, u);
+                for (int u = 0; u < T::KS; ++u)
 #pragma unroll
-            for (int u = 0; u < T::KS; ++u)
+                    for (int qb = 0; qb < QB; ++qb)
+                        o[qb][u % T::DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            vfr[u], pk[(T::KB - 1) & 1][qb][u / T::DB], o[qb][u % T::DB], 0, 0, 0);
+            } else {
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    o[qb][u % T::DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[u], pk[(T::KB - 1) & 1][qb][u / T::DB],
-                                                                              o[qb][u % T::DB], 0, 0, 0);
+                for (int u = 0; u < T::KS; ++u) fr[u] = read_v(T::KB - 1, u);
+#pragma unroll
+                for (int u = 0; u < T::KS; ++u)
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        o[qb][u % T::DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            fr[u], pk[(T::KB - 1) & 1][qb][u / T::DB], o[qb][u % T::DB], 0, 0, 0);
+            }
         }
     };
 
@@ -475,11 +631,27 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
         // S(0), then the K fragments of sub-block 1 for the first iteration
+        if constexpr (F8) {
 #pragma unroll
-        for (int u = 0; u < T::KS; ++u) fr[u] = read_k(0, u);
-        qk(fr, sc[0]);
+            for (int t = 0; t < T::KQ; ++t) kf8[t] = read_k8(0, t);
 #pragma unroll
-        for (int u = 0; u < T::KS; ++u) fr[u] = read_k(1, u);
+            for (int qb = 0; qb < QB; ++qb) {
+                const f32x16 zero = {};
+#pragma unroll
+                for (int t = 0; t < T::KQ; ++t) sc[0][qb] = mfma8(kf8[t], qf8[qb][t], t == 0 ? zero : sc[0][qb]);
+            }
+#pragma unroll
+            for (int t = 0; t < T::KQ; ++t) kf8[t] = read_k8(1, t);
+            // finite V rows for the zero-weight P.V of sub-block -1
+#pragma unroll
+            for (int u = 0; u < T::KS; ++u) vfr[u] = read_v(0, u);
+        } else {
+#pragma unroll
+            for (int u = 0; u < T::KS; ++u) fr[u] = read_k(0, u);
+            qk(fr, sc[0]);
+#pragma unroll
+            for (int u = 0; u < T::KS; ++u) fr[u] = read_k(1, u);
+        }
         // Sub-block 0 has no predecessor: its P.V slots multiply zero
         // weights with loaded (finite) V rows instead, which keeps one
         // branch-free body for every stage.
@@ -502,13 +674,13 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
         const int32_t nfree = min(jmask, nkt - 1);
         int32_t j = 0;
         for (; j < nfree; ++j) {
-            stage(j, kbuf, vnext, kbuf ? -T::SBYTES : T::SBYTES, (vbuf - vprev) * T::SBYTES, std::false_type{},
+            stage(j, kbuf, vnext, kbuf ? -T::KSBYTES : T::KSBYTES, (vbuf - vprev) * T::SBYTES, std::false_type{},
                   std::false_type{});
             advance();
         }
         if constexpr (CAUSAL) {
             for (; j + 1 < nkt; ++j) {
-                stage(j, kbuf, vnext, kbuf ? -T::SBYTES : T::SBYTES, (vbuf - vprev) * T::SBYTES, std::false_type{},
+                stage(j, kbuf, vnext, kbuf ? -T::KSBYTES : T::KSBYTES, (vbuf - vprev) * T::SBYTES, std::false_type{},
                       std::true_type{});
                 advance();
             }
@@ -538,7 +710,7 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
                 }
             if (hf == 0 && a.lse != nullptr) {
                 // natural-log LSE: m*scale + ln l (any reference m gives the same value)
-                const float lse = l_tot > 0.f ? m_i[qb] * a.scale + __logf(l_tot) : -INFINITY;
+                const float lse = l_tot > 0.f ? m_i[qb] * lse_scale + __logf(l_tot) : -INFINITY;
                 a.lse[(int64_t)h * a.lse_head + q_tok0 + row + gseg * a.lse_seg] = lse;
             }
         }
@@ -576,16 +748,27 @@ template <int D, int QB, int NW, int BN>
 hipError_t launch_cfg(const AvfLaunchArgs& a, hipStream_t stream) {
     // grid: the exact tile count, or with a device plan the host's bound
     const dim3 grid((uint32_t)a.num_tiles), block(NW * 64);
+    if (a.q8) {
+        if constexpr (D % 64 == 0) {
+            if (a.causal)
+                hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true, false, true>), grid, block, 0, stream, a);
+            else
+                hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false, false, true>), grid, block, 0, stream, a);
+            return hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
     if (a.dev_plan) {
         if (a.causal)
-            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true, true>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true, true, false>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false, true>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false, true, false>), grid, block, 0, stream, a);
     } else {
         if (a.causal)
-            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true, false>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true, false, false>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false, false>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false, false, false>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -35,6 +35,12 @@ struct AvfLaunchArgs {
     const int32_t* dev_plan;
     const int32_t* cu_q;
     const int32_t* cu_k;
+    // 8-bit score product: packed E4M3 codes of q and k ([tokens, H, D]
+    // bytes) and their per-head amax (fp32 bits: H words for q, then H for
+    // k); NULL for the bf16 path
+    const uint8_t* q8;
+    const uint8_t* k8;
+    const uint32_t* amax8;
     float scale_log2e;  // softmax_scale * log2(e): logits in base-2 units
     float scale;        // softmax_scale: the LSE is reported in natural-log units
     int32_t num_heads;
