@@ -395,3 +395,33 @@ def test_async_rejects_host_errors_before_any_hip_call():
     lay_bad = layout(o_row=8, o_head=8)
     bad = (P, P, P, cq, cq, 2, 2, 64, 6, 7, ctypes.byref(lay_bad), 0.125, 0, P, 256, P, P, None)
     assert L.attn_varlen_fwd_async(*bad) == _binding.EINVAL
+
+
+# ---------------------------------------------------------------- low-precision forward (host side)
+
+def test_fp8_workspace_layout():
+    q8, k8 = avf.fp8_workspace_offsets(100, 120, 2, 64)
+    assert (q8, k8) == (256, 256 + 100 * 2 * 64)
+    assert avf.fp8_workspace_bytes(100, 120, 2, 64) == k8 + -(-(120 * 2 * 64) // 256) * 256
+    # sizes past 2^31 bytes are fine (64-bit arithmetic throughout)
+    big = avf.fp8_workspace_bytes(410923, 410923, 56, 128)
+    assert big == 512 + 2 * (-(-(410923 * 56 * 128) // 256) * 256) and big > 2 ** 32  # 2*56 amax words -> 512
+    for D in (96, 80):
+        with pytest.raises(avf.AttnVarlenError):
+            avf.fp8_workspace_bytes(10, 10, 2, D)
+
+
+def test_fp8_rejects_host_errors_before_any_hip_call():
+    L = avf.lib()
+    lay = layout()
+    cq = (ctypes.c_int32 * 3)(0, 4, 10)
+    ck = (ctypes.c_int32 * 3)(0, 5, 12)
+    W = 1 << 20  # 256-byte aligned fake workspace address
+    def call(D=64, ws=W, nbytes=1 << 20, lay_=lay, flags=0):
+        return L.attn_varlen_fwd_fp8_hostcu(P, P, P, cq, ck, 2, 2, D, 6, 7, ctypes.byref(lay_), 0.125, flags, ws,
+                                            nbytes, P, P, None)
+    assert call(D=96, lay_=layout(D=96)) == _binding.EUNSUPPORTED
+    assert call(ws=None) == _binding.ENULL
+    assert call(ws=W + 16) == _binding.EALIGN
+    assert call(nbytes=100) == _binding.EINVAL
+    assert call(flags=8) == _binding.EINVAL
