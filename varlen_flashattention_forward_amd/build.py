@@ -20,7 +20,8 @@ CSRC = PKG / "csrc"
 ROOT = PKG.parent
 LIB = Path(os.environ.get("AVF_LIB_OUT", PKG / "libattn_varlen.so"))
 BUILD_DIR = Path(os.environ.get("AVF_BUILD_DIR", PKG / "_build"))
-SOURCES = ["avf_api.hip", "avf_kernel.hip", "avf_bwd_kernel.hip", "avf_planner.hip", "avf_quant.hip"]
+SOURCES = ["avf_api.hip", "avf_kernel.hip", "avf_bwd_kernel.hip", "avf_bwd_dkdv_small.hip", "avf_planner.hip",
+           "avf_quant.hip"]
 ARCH = os.environ.get("AVF_OFFLOAD_ARCH", "gfx950")
 
 
@@ -36,10 +37,10 @@ def common_flags(src: str = "avf_kernel.hip") -> list:
              f"-I{ROOT / 'include'}", f"-I{CSRC}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
     if src != "avf_bwd_kernel.hip":
-        # forward: MFMA accumulators in architectural VGPRs, so the softmax
-        # rescale and epilogue touch them without AGPR<->VGPR copies. The
-        # backward kernels keep more accumulators than 256 VGPRs hold and
-        # leave the choice to the compiler.
+        # MFMA results in architectural VGPRs, so the softmax (and rescale,
+        # epilogue) read them without AGPR<->VGPR copies. avf_bwd_kernel.hip
+        # holds the head_dim-128 dK/dV kernel, whose accumulators exceed 256
+        # VGPRs, and leaves the choice to the compiler.
         flags += ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
     return flags + extra_flags()
 

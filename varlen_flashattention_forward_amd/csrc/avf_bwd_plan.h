@@ -50,6 +50,8 @@ struct AvfBwdArgs {
 // dK/dV tile and query rows per dQ tile (-1 for an unsupported head_dim).
 hipError_t avf_bwd_preprocess_launch(const AvfPreArgs& args, int32_t head_dim, hipStream_t stream);
 hipError_t avf_bwd_dkdv_launch(const AvfBwdArgs& args, int32_t head_dim, hipStream_t stream);
+// head_dim 64 and 96 (a separate compilation unit; called by avf_bwd_dkdv_launch)
+hipError_t avf_bwd_dkdv_launch_small(const AvfBwdArgs& args, int32_t head_dim, hipStream_t stream);
 hipError_t avf_bwd_dq_launch(const AvfBwdArgs& args, int32_t head_dim, hipStream_t stream);
 int32_t avf_bwd_block_n(int32_t head_dim);
 int32_t avf_bwd_block_m(int32_t head_dim);
