@@ -162,3 +162,16 @@ def test_sync_free_in_a_hip_graph():
         torch.cuda.synchronize()
         assert torch.equal(o, ref_o), rep
         assert torch.equal(l[:, :w.total_q], ref_l[:, :w.total_q]), rep
+
+
+def test_sync_free_strided_views():
+    """The page's [N, 9728] layout through the sync-free entry: equal to the
+    host-planned path on the same views."""
+    announce("sync-free strided 9728")
+    w = custom("async_strided", 16, 96, [0, 700, 1300, 2100], std=0.1, layout="stride9728", outer_stride=9728)
+    t = make_inputs(w, "cuda", seed=6)
+    a_o, a_l = host_planned(t, w)
+    b_o, b_l, ws = sync_free(t, w)
+    torch.cuda.synchronize()
+    assert avf.async_status(ws) == 0
+    assert torch.equal(a_o, b_o) and torch.equal(a_l[:, :w.total_q], b_l[:, :w.total_q])

@@ -135,3 +135,43 @@ def test_fp8_full_size_sampled_heads():
     gl = l[heads][:, rows].t().cpu().numpy()
     st = compare(go, gl, ro, rl, "fp8 dense_77k")
     print(f"[fp8 dense_77k] {st}", flush=True)
+
+
+def test_fp8_strided_views_equal_contiguous():
+    """q, k, v as views of wider buffers (row stride 3*H*D + 64): the same
+    codes and outputs as their contiguous copies."""
+    announce("fp8 strided views")
+    w = custom("fp8_strided", 4, 128, [0, 333, 900], [0, 500, 1200], std=1.0)
+    H, D = 4, 128
+    g = torch.Generator(device="cuda").manual_seed(31)
+    def view(n):
+        buf = torch.randn((n, 3 * H * D + 64), dtype=torch.bfloat16, device="cuda", generator=g)
+        return buf[:, 64:64 + H * D].view(n, H, D)
+    t = make_inputs(w, "cuda", seed=31)
+    t["q"], t["k"], t["v"] = view(w.total_q), view(w.total_k), view(w.total_k)
+    a, al, _ = run_fp8(t, w)
+    a, al = a.clone(), al.clone()
+    for n in ("q", "k", "v"):
+        t[n] = t[n].contiguous()
+    b, bl, _ = run_fp8(t, w)
+    assert torch.equal(a, b) and torch.equal(al[:, :w.total_q], bl[:, :w.total_q])
+
+
+def test_fp8_many_segments_span_launches():
+    """300 segments: the plan splits them over launches of 128; codes index
+    absolute token rows across launches."""
+    announce("fp8 300 segments")
+    rng = np.random.default_rng(32)
+    lens_q = [0 if rng.random() < 0.1 else int(rng.integers(1, 150)) for _ in range(300)]
+    lens_k = [0 if rng.random() < 0.1 else int(rng.integers(1, 150)) for _ in range(300)]
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(int).tolist()
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(int).tolist()
+    w = custom("fp8_many", 2, 64, cu_q, cu_k, std=1.0)
+    t = make_inputs(w, "cuda", seed=32)
+    o, l, _ = run_fp8(t, w)
+    rows = sample_rows(w, 4, edge=1)
+    ro, rl = fp8_oracle.attn_varlen_fwd_fp8(cpu_bits(t["q"]), cpu_bits(t["k"]), cpu_bits(t["v"]), w.cu_q, w.cu_k,
+                                            f32(w.softmax_scale), rows=rows)
+    idx = torch.tensor(rows, device="cuda")
+    compare(o.index_select(0, idx).float().cpu().numpy(), l[:, :w.total_q].index_select(1, idx).t().cpu().numpy(),
+            ro, rl, "fp8 many segments")
