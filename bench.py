@@ -82,6 +82,28 @@ def cpu_baseline(w, t, rows_per_segment: int):
                       f"{'visible ' if w.causal else ''}segments (C fp64 oracle, {dt:.1f} s, {flops / 1e9:.1f} GFLOP)"}
 
 
+def cpu_baseline_fp8(w, t, rows_per_segment: int, heads: int = 4):
+    """The fp8 oracle on sampled rows of the first `heads` heads (its scales
+    are per head, so those heads quantize on their own)."""
+    import numpy as np
+
+    from oracle import fp8_oracle
+    from varlen_flashattention_forward_amd.workloads import sample_rows
+
+    rows = sample_rows(w, rows_per_segment, edge=min(8, rows_per_segment // 2))
+    hs = list(range(min(heads, w.num_heads)))
+    q, k, v = (t[n][:, hs].contiguous().cpu() for n in ("q", "k", "v"))
+    flops = sum(4 * w.visible_keys(r) * w.head_dim * len(hs) for r in rows)
+    t0 = time.perf_counter()
+    fp8_oracle.attn_varlen_fwd_fp8(q, k, v, w.cu_q, w.cu_k, float(np.float32(w.softmax_scale)), rows=rows,
+                                   causal=w.causal)
+    dt = time.perf_counter() - t0
+    import oracle
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.default_threads(), "kind": "oracle",
+            "sample": f"{len(rows)} query rows x {len(hs)} heads of {w.name} with those heads' E4M3 "
+                      f"quantization (numpy fp64 oracle, {dt:.1f} s, {flops / 1e9:.1f} GFLOP)"}
+
+
 def cpu_baseline_bwd(w, t, dout, rows_per_segment: int):
     import numpy as np
 
@@ -207,6 +229,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--async", dest="use_async", action="store_true",
                     help="time the sync-free entry point (device planner, no host read-back)")
+    ap.add_argument("--batched", action="store_true",
+                    help="time the batched-dense entry attn_fwd on [segments, S, H, D] views (uniform segments)")
     ap.add_argument("--fp8", action="store_true",
                     help="time the low-precision forward (E4M3 q and k, 8-bit score product)")
     ap.add_argument("--backward", action="store_true", help="time the backward pass (default workload bwd_9728)")
@@ -254,8 +278,21 @@ def main() -> int:
         ws8 = torch.empty(avf.fp8_workspace_bytes(w.total_q, w.total_k, w.num_heads, w.head_dim), dtype=torch.uint8,
                           device=dev)
 
+    if args.batched:
+        Ls = {w.cu_q[b + 1] - w.cu_q[b] for b in range(w.num_segments)}
+        Lk = {w.cu_k[b + 1] - w.cu_k[b] for b in range(w.num_segments)}
+        if len(Ls) != 1 or len(Lk) != 1:
+            print(f"--batched needs uniform segments ({w.name} is not)", file=sys.stderr)
+            return 2
+        W, Sq, Sk = w.num_segments, Ls.pop(), Lk.pop()
+        qb, kb, vb = (t[n].view(W, -1, w.num_heads, w.head_dim) for n in ("q", "k", "v"))
+        ob = t["out"].view(W, Sq, w.num_heads, w.head_dim)
+        lb = torch.empty((W, w.num_heads, Sq), dtype=torch.float32, device=dev)
+
     def step():
-        if args.fp8:
+        if args.batched:
+            avf.attn_fwd(qb, kb, vb, softmax_scale=w.softmax_scale, causal=w.causal, out=ob, lse=lb)
+        elif args.fp8:
             avf.attn_varlen_fwd_fp8(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
                                     workspace=ws8, softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"],
                                     causal=w.causal)
@@ -288,7 +325,10 @@ def main() -> int:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        if args.fp8:
+        if args.batched:
+            avf.attn_fwd(qb, kb, vb, softmax_scale=w.softmax_scale, causal=w.causal, out=ob, lse=lb,
+                         stream=stream.cuda_stream)
+        elif args.fp8:
             avf.attn_varlen_fwd_fp8(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
                                     workspace=ws8, softmax_scale=w.softmax_scale, out=t["out"], lse=t["lse"],
                                     cu_seqlens_q_host=cu_q, cu_seqlens_k_host=cu_k, stream=stream.cuda_stream,
@@ -321,7 +361,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
-        cpu = cpu_baseline(w, t, args.cpu_rows)
+        cpu = cpu_baseline_fp8(w, t, args.cpu_rows) if args.fp8 else cpu_baseline(w, t, args.cpu_rows)
         log(f"[bench] cpu baseline {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
 
     rec = {
@@ -344,7 +384,7 @@ def main() -> int:
                    "max_seqlen_q": w.max_seqlen_q, "max_seqlen_k": w.max_seqlen_k,
                    "layout": w.layout, "causal": w.causal, "flops_per_step": flops,
                    "workgroups": wgs, "block_m": avf.block_m(w.head_dim),
-                   "entry": ("attn_varlen_fwd_fp8" if args.fp8 else
+                   "entry": ("attn_fwd_batched" if args.batched else "attn_varlen_fwd_fp8" if args.fp8 else
                              "attn_varlen_fwd_async" if args.use_async else "attn_varlen_fwd")},
         "roofline": roofline,
         "cpu_baseline": cpu,
