@@ -144,6 +144,19 @@ int32_t check_with_cu(const int32_t* cu_q, int32_t B, int32_t H, int32_t D,
     return ATTN_VARLEN_OK;
 }
 
+// Device cu_seqlens (B+1 entries each) copied to the host on `s` and waited
+// for: the one synchronisation of the entry points that take device cu.
+int32_t read_cu(const int32_t* cu_q_dev, const int32_t* cu_k_dev, int32_t B, hipStream_t s, std::vector<int32_t>& cu) {
+    if (!cu_q_dev || !cu_k_dev) return fail(ATTN_VARLEN_ENULL, "cu_seqlens_q/k must be non-NULL");
+    cu.assign((size_t)2 * (B + 1), 0);
+    hipError_t e = hipMemcpyAsync(cu.data(), cu_q_dev, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(cu.data() + B + 1, cu_k_dev, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "reading cu_seqlens failed: %s", hipGetErrorString(e));
+    return ATTN_VARLEN_OK;
+}
+
 int32_t validate_all(const void* q, const void* k, const void* v, const int32_t* cu_q,
                      const int32_t* cu_k, int32_t B, int32_t H, int32_t D, int32_t max_q,
                      int32_t max_k, const attn_varlen_layout* st, float scale, const void* out,
@@ -283,14 +296,9 @@ int32_t attn_varlen_fwd_ex(const void* q, const void* k, const void* v, const in
     if (rc != ATTN_VARLEN_OK) return rc;
     rc = check_scalars(q, k, v, B, H, D, max_q, max_k, st, scale, out, lse);
     if (rc != ATTN_VARLEN_OK || B == 0) return rc;
-    if (!cu_q_dev || !cu_k_dev) return fail(ATTN_VARLEN_ENULL, "cu_seqlens_q/k must be non-NULL");
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    std::vector<int32_t> cu((size_t)2 * (B + 1));
-    hipError_t e = hipMemcpyAsync(cu.data(), cu_q_dev, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(cu.data() + B + 1, cu_k_dev, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "reading cu_seqlens failed: %s", hipGetErrorString(e));
+    std::vector<int32_t> cu;
+    if ((rc = read_cu(cu_q_dev, cu_k_dev, B, s, cu)) != ATTN_VARLEN_OK) return rc;
     const int32_t* cq = cu.data();
     const int32_t* ck = cu.data() + B + 1;
     rc = check_cu(cq, ck, B, max_q, max_k, st);
@@ -698,14 +706,9 @@ int32_t attn_varlen_bwd(const void* q, const void* k, const void* v, const void*
     g_last_error.clear();
     int32_t rc = bwd_check_scalars(q, k, v, o, g, lse, B, H, D, max_q, max_k, st, scale, flags, delta, dq, dk, dv);
     if (rc != ATTN_VARLEN_OK || B == 0) return rc;
-    if (!cu_q_dev || !cu_k_dev) return fail(ATTN_VARLEN_ENULL, "cu_seqlens_q/k must be non-NULL");
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    std::vector<int32_t> cu((size_t)2 * (B + 1));
-    hipError_t e = hipMemcpyAsync(cu.data(), cu_q_dev, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(cu.data() + B + 1, cu_k_dev, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "reading cu_seqlens failed: %s", hipGetErrorString(e));
+    std::vector<int32_t> cu;
+    if ((rc = read_cu(cu_q_dev, cu_k_dev, B, s, cu)) != ATTN_VARLEN_OK) return rc;
     const int32_t* cq = cu.data();
     const int32_t* ck = cu.data() + B + 1;
     rc = bwd_check_cu(cq, ck, B, H, D, max_q, max_k, st);
@@ -949,14 +952,9 @@ int32_t attn_varlen_fwd_fp8(const void* q, const void* k, const void* v, const i
     rc = check_scalars(q, k, v, B, H, D, max_q, max_k, st, scale, out, lse);
     if (rc != ATTN_VARLEN_OK || B == 0) return rc;
     if ((rc = fp8_check(D, workspace)) != ATTN_VARLEN_OK) return rc;
-    if (!cu_q_dev || !cu_k_dev) return fail(ATTN_VARLEN_ENULL, "cu_seqlens_q/k must be non-NULL");
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    std::vector<int32_t> cu((size_t)2 * (B + 1));
-    hipError_t e = hipMemcpyAsync(cu.data(), cu_q_dev, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(cu.data() + B + 1, cu_k_dev, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "reading cu_seqlens failed: %s", hipGetErrorString(e));
+    std::vector<int32_t> cu;
+    if ((rc = read_cu(cu_q_dev, cu_k_dev, B, s, cu)) != ATTN_VARLEN_OK) return rc;
     const int32_t* cq = cu.data();
     const int32_t* ck = cu.data() + B + 1;
     rc = check_cu(cq, ck, B, max_q, max_k, st);
