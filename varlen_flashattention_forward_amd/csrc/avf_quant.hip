@@ -31,20 +31,25 @@ __global__ void avf_amax_clear(uint32_t* amax, int32_t n) {
     if (i < n) amax[i] = 0u;
 }
 
-// kernel 2: one workgroup per (chunk of 64 rows, head). D/8 lanes per row,
-// 16 bytes each; wave max by shuffles, then one atomic max per wave on the
-// float's bit pattern (non-negative floats order like their bits).
+// kernel 2: one workgroup per (chunk of kAmaxChunk rows, head). D/8 lanes
+// per row, 16 bytes each; the workgroup's max by shuffles within each wave
+// and LDS across waves, then ONE atomic max per workgroup on the float's bit
+// pattern (non-negative floats order like their bits). All workgroups of a
+// head update one word, so the atomics are kept few.
+constexpr int kAmaxChunk = 1024;
+
 template <int D>
 __global__ void __launch_bounds__(256) avf_amax_kernel(const void* x, int64_t rows, int64_t row_stride,
                                                        int64_t head_stride, uint32_t* amax) {
     constexpr int LPR = D / 8;            // lanes per row
     constexpr int RPP = 256 / LPR;        // rows per pass
+    __shared__ float wmax[4];
     const int64_t h = blockIdx.y;
-    const int64_t r0 = (int64_t)blockIdx.x * 64;
+    const int64_t r0 = (int64_t)blockIdx.x * kAmaxChunk;
     const int tid = threadIdx.x;
     const int c = tid % LPR;
     float m = 0.f;
-    for (int p = tid / LPR; p < 64; p += RPP) {
+    for (int p = tid / LPR; p < kAmaxChunk; p += RPP) {
         const int64_t r = r0 + p;
         if (r < rows) {
             const bf16x8 v = *reinterpret_cast<const bf16x8*>((const char*)x + 2 * (r * row_stride + h * head_stride) +
@@ -55,7 +60,12 @@ __global__ void __launch_bounds__(256) avf_amax_kernel(const void* x, int64_t ro
     }
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s));
-    if ((tid & 63) == 0) atomicMax(amax + h, __float_as_uint(m));
+    if ((tid & 63) == 0) wmax[tid >> 6] = m;
+    __syncthreads();
+    if (tid == 0) {
+        m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+        atomicMax(amax + h, __float_as_uint(m));
+    }
 }
 
 // kernel 3: codes. One thread per 8 elements (16 input bytes -> 8 codes).
@@ -88,11 +98,12 @@ template <int D>
 hipError_t quantize(const void* x, int64_t rows, int32_t H, int64_t row_stride, int64_t head_stride, uint32_t* amax,
                     uint8_t* codes, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    // amax in row chunks of 2^24 rows (2^18 workgroups per head and launch)
+    // amax in row chunks of 2^24 rows per launch
     constexpr int64_t kAmaxRows = (int64_t)1 << 24;
     for (int64_t r0 = 0; r0 < rows; r0 += kAmaxRows) {
         const int64_t n = std::min(kAmaxRows, rows - r0);
-        hipLaunchKernelGGL((avf_amax_kernel<D>), dim3((uint32_t)((n + 63) / 64), (uint32_t)H), dim3(256), 0, s,
+        hipLaunchKernelGGL((avf_amax_kernel<D>), dim3((uint32_t)((n + kAmaxChunk - 1) / kAmaxChunk), (uint32_t)H),
+                           dim3(256), 0, s,
                            (const char*)x + 2 * r0 * row_stride, n, row_stride, head_stride, amax);
     }
     // codes in row chunks of at most 2^30 threads per launch
