@@ -344,19 +344,31 @@ def main() -> int:
         durs.append((e0, e1))
     torch.cuda.synchronize()
     kms = sum(a.elapsed_time(b) for a, b in durs) / len(durs)
-    launches, wgs = avf.grid_plan(w.cu_q, w.num_heads, w.head_dim)
+    # the 8-bit forward always takes the general configuration
+    max_k_cfg = 1 << 30 if args.fp8 else w.max_seqlen_k
+    launches, wgs = avf.grid_plan(w.cu_q, w.num_heads, w.head_dim, max_k_cfg)
     if args.use_async:
-        launches, wgs = 1, avf.async_grid(w.total_q, w.num_segments, w.num_heads, w.head_dim, w.max_seqlen_q)
+        launches, wgs = 1, avf.async_grid(w.total_q, w.num_segments, w.num_heads, w.head_dim, w.max_seqlen_q,
+                                          w.max_seqlen_k)
     achieved = flops / launches / (kms / launches / 1e3) / 1e12
     log(f"[bench] kernel: {kms:.3f} ms/call over {launches} launch(es), {wgs} workgroups, {achieved:.1f} TFLOP/s")
     traffic = traffic_for(w.name)
     peak = PEAK_FP8_QK_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
     if args.fp8:
         traffic = None  # the counters were taken on the bf16 kernel
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic,
-                "kernel_ms": round(kms / launches, 4), "algorithmic_flops_per_launch": flops // launches,
-                "algorithmic_bytes_per_launch": w.algorithmic_bytes() // launches}
+    nbytes = w.algorithmic_bytes()
+    # the bound: MFMA above the ridge (peak FLOP/s over peak HBM bytes/s), HBM below it
+    if flops / nbytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4)}
+    else:
+        gbs = nbytes / launches / (kms / launches / 1e3) / 1e9
+        log(f"[bench] below the ridge ({flops / nbytes:.0f} flop/B): {gbs:.1f} GB/s of algorithmic bytes")
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    roofline.update({"traffic": traffic, "kernel_ms": round(kms / launches, 4),
+                     "algorithmic_flops_per_launch": flops // launches,
+                     "algorithmic_bytes_per_launch": nbytes // launches})
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -383,7 +395,7 @@ def main() -> int:
                    "segments": w.num_segments, "total_q": w.total_q, "total_k": w.total_k,
                    "max_seqlen_q": w.max_seqlen_q, "max_seqlen_k": w.max_seqlen_k,
                    "layout": w.layout, "causal": w.causal, "flops_per_step": flops,
-                   "workgroups": wgs, "block_m": avf.block_m(w.head_dim),
+                   "workgroups": wgs, "block_m": avf.block_m(w.head_dim, max_k_cfg),
                    "entry": ("attn_fwd_batched" if args.batched else "attn_varlen_fwd_fp8" if args.fp8 else
                              "attn_varlen_fwd_async" if args.use_async else "attn_varlen_fwd")},
         "roofline": roofline,

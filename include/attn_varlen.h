@@ -127,10 +127,27 @@ int32_t attn_varlen_validate(const void* q, const void* k, const void* v,
                              const void* out, const float* lse);
 
 /*
- * Query rows per tile (BM) the library uses for head_dim, or
+ * Query rows per tile (BM) of the general configuration for head_dim (the
+ * one used when max_seqlen_k exceeds attn_varlen_one_stage_keys()), or
  * ATTN_VARLEN_EUNSUPPORTED.
  */
 int32_t attn_varlen_block_m(int32_t head_dim);
+
+/*
+ * Query rows per tile the bf16 forward uses for a call with this
+ * max_seqlen_k. When no key segment can be longer than one K/V stage
+ * (max_seqlen_k <= attn_varlen_one_stage_keys(), 128), a tile needs LDS for
+ * one stage only, and the forward switches to smaller workgroups that share a
+ * CU in pairs. That is the short-segment, HBM-bound regime: with one segment
+ * of keys per tile there is no K/V reuse to pipeline. The choice follows the
+ * caller's max_seqlen_k, which every entry point validates against the
+ * segments (on the host, or in the device planner), so it never depends on
+ * values the host cannot see. The 8-bit forward always uses the general
+ * configuration. Returns ATTN_VARLEN_EUNSUPPORTED for an unsupported
+ * head_dim and ATTN_VARLEN_EINVAL for max_seqlen_k < 0.
+ */
+int32_t attn_varlen_block_m_for(int32_t head_dim, int32_t max_seqlen_k);
+int32_t attn_varlen_one_stage_keys(void);
 
 /*
  * Exact tile count H * sum_b ceil(Lq_b / block_m) for host cu_seqlens_q
@@ -142,13 +159,14 @@ int64_t attn_varlen_count_tiles(const int32_t* cu_seqlens_q_host, int32_t num_se
 
 /*
  * Number of kernel launches and workgroups attn_varlen_fwd would use for
- * these host cu_seqlens (segments are split into launches of at most
- * attn_varlen_segments_per_launch() segments; each launch's grid is exactly
- * its tile count). Writes the totals to *launches and *workgroups.
+ * these host cu_seqlens_q and this max_seqlen_k (which picks the tile
+ * height, attn_varlen_block_m_for). Segments are split into launches of at
+ * most attn_varlen_segments_per_launch() segments; each launch's grid is
+ * exactly its tile count. Writes the totals to *launches and *workgroups.
  */
 int32_t attn_varlen_grid_plan(const int32_t* cu_seqlens_q_host, int32_t num_segments,
-                              int32_t num_heads, int32_t head_dim, int64_t* launches,
-                              int64_t* workgroups);
+                              int32_t num_heads, int32_t head_dim, int32_t max_seqlen_k,
+                              int64_t* launches, int64_t* workgroups);
 int32_t attn_varlen_segments_per_launch(void);
 
 /*
@@ -299,7 +317,8 @@ int32_t attn_varlen_async_status(const void* workspace, void* stream, int32_t* s
 
 /* Workgroups attn_varlen_fwd_async launches for these host-known values. */
 int32_t attn_varlen_async_grid(int64_t q_tokens, int32_t num_segments, int32_t num_heads,
-                               int32_t head_dim, int32_t max_seqlen_q, int64_t* workgroups);
+                               int32_t head_dim, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int64_t* workgroups);
 
 /*
  * ---- Low-precision forward (8-bit score product) ---------------------------

@@ -95,7 +95,8 @@ def test_sync_free_grid_smaller_than_tile_count_loops():
     announce("sync-free looping grid")
     w = custom("loop", 64, 64, [0, 33000], std=1.0)
     bm = avf.block_m(64)
-    assert avf.count_tiles(w.cu_q, 64, bm) > avf.async_grid(w.total_q, 1, 64, 64, w.max_seqlen_q) == 8192
+    assert avf.count_tiles(w.cu_q, 64, bm) > avf.async_grid(w.total_q, 1, 64, 64, w.max_seqlen_q,
+                                                            w.max_seqlen_k) == 8192
     t = make_inputs(w, "cuda", seed=3)
     a_o, a_l = host_planned(t, w)
     b_o, b_l, ws = sync_free(t, w)

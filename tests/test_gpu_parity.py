@@ -106,7 +106,7 @@ def test_many_segments_multiple_launches():
     cq = np.concatenate([[0], np.cumsum(lq)]).tolist()
     ck = np.concatenate([[0], np.cumsum(lk)]).tolist()
     w = custom("many_segments", 2, 64, cq, ck, std=1.0)
-    launches, _ = avf.grid_plan(w.cu_q, w.num_heads, w.head_dim)
+    launches, _ = avf.grid_plan(w.cu_q, w.num_heads, w.head_dim, w.max_seqlen_k)
     assert launches >= 3
     announce(f"many segments B={n} launches={launches}")
     t = make_inputs(w, DEV, seed=5)

@@ -84,9 +84,11 @@ def test_tile_count_matches_pages_valid_tiles():
 
 def test_our_grid_is_exact_for_every_workload():
     for w in WORKLOADS.values():
-        bm = avf.block_m(w.head_dim)
+        bm = avf.block_m(w.head_dim, w.max_seqlen_k)
+        # segments of at most one K/V stage take the one-stage configuration (128-row tiles)
+        assert bm == (128 if w.max_seqlen_k <= avf.one_stage_keys() else avf.block_m(w.head_dim))
         exact = w.num_heads * sum(math.ceil((b - a) / bm) for a, b in zip(w.cu_q[:-1], w.cu_q[1:]))
-        launches, wgs = avf.grid_plan(w.cu_q, w.num_heads, w.head_dim)
+        launches, wgs = avf.grid_plan(w.cu_q, w.num_heads, w.head_dim, w.max_seqlen_k)
         assert wgs == exact == avf.count_tiles(w.cu_q, w.num_heads, bm)
         assert launches == 1
 
@@ -98,10 +100,12 @@ def test_grid_plan_splits_long_segment_lists():
     cu = [0]
     for x in lens:
         cu.append(cu[-1] + x)
-    launches, wgs = avf.grid_plan(cu, 3, 128)
-    bm = avf.block_m(128)
-    assert wgs == 3 * sum(math.ceil(x / bm) for x in lens)
-    assert launches == math.ceil(len(lens) / spl)
+    for max_k in (max(lens), 128):
+        launches, wgs = avf.grid_plan(cu, 3, 128, max_k)
+        bm = avf.block_m(128, max_k)
+        assert bm == (avf.block_m(128) if max_k > 128 else 128)
+        assert wgs == 3 * sum(math.ceil(x / bm) for x in lens)
+        assert launches == math.ceil(len(lens) / spl)
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -207,11 +211,19 @@ def test_validate_never_needs_lse_head_with_one_head():
 
 
 def test_block_m_and_unsupported_dims():
+    assert avf.one_stage_keys() == 128
     for d in (64, 96, 128):
         bm = avf.block_m(d)
         assert bm > 0 and bm % 32 == 0
+        # max_seqlen_k picks the configuration: one stage up to 128 keys
+        assert avf.block_m(d, 0) == avf.block_m(d, 1) == avf.block_m(d, 128) == 128
+        assert avf.block_m(d, 129) == avf.block_m(d, 1 << 30) == bm
+        with pytest.raises(avf.AttnVarlenError, match="EINVAL"):
+            avf.block_m(d, -1)
     with pytest.raises(avf.AttnVarlenError):
         avf.block_m(100)
+    with pytest.raises(avf.AttnVarlenError):
+        avf.block_m(100, 64)
 
 
 def test_forward_rejects_cpu_tensors_before_any_hip_call():
@@ -365,9 +377,10 @@ def test_async_grid_bounds_the_tile_count(seed):
         H, D = rng.choice([1, 3, 56]), rng.choice([64, 96, 128])
         q_tokens = cu[-1] + rng.randint(0, 500)
         max_q = max(lens) + rng.randint(0, 100)
-        bm = avf.block_m(D)
+        max_k = rng.choice([0, 64, 128, 129, 5000])
+        bm = avf.block_m(D, max_k)
         tiles = avf.count_tiles(cu, H, bm)
-        g = avf.async_grid(q_tokens, B, H, D, max_q)
+        g = avf.async_grid(q_tokens, B, H, D, max_q, max_k)
         assert g % 8 == 0 and g <= 8192
         assert g >= min(tiles, 8192)
         bound = H * min(math.ceil((q_tokens + B * (bm - 1)) / bm), B * math.ceil(max_q / bm))

@@ -30,6 +30,7 @@ EXPORTED_SYMBOLS = (
     "attn_varlen_bwd_grid_plan", "attn_varlen_async_workspace_bytes", "attn_varlen_fwd_async",
     "attn_varlen_async_status", "attn_varlen_async_grid", "attn_varlen_fp8_workspace_bytes",
     "attn_varlen_fp8_workspace_offsets", "attn_varlen_fwd_fp8", "attn_varlen_fwd_fp8_hostcu",
+    "attn_varlen_block_m_for", "attn_varlen_one_stage_keys",
 )
 
 CAUSAL = 1  # ATTN_VARLEN_CAUSAL
@@ -117,7 +118,7 @@ def lib():
         L.attn_varlen_async_status.restype = ctypes.c_int32
         L.attn_varlen_async_status.argtypes = [_vp, _vp, _i32p]
         L.attn_varlen_async_grid.restype = ctypes.c_int32
-        L.attn_varlen_async_grid.argtypes = [ctypes.c_int64] + [ctypes.c_int32] * 4 + [_i64p]
+        L.attn_varlen_async_grid.argtypes = [ctypes.c_int64] + [ctypes.c_int32] * 5 + [_i64p]
         L.attn_varlen_fp8_workspace_bytes.restype = ctypes.c_int64
         L.attn_varlen_fp8_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
         L.attn_varlen_fp8_workspace_offsets.restype = ctypes.c_int32
@@ -129,10 +130,15 @@ def lib():
             f.argtypes = fwd_args[:12] + [ctypes.c_uint32, _vp, ctypes.c_int64] + fwd_args[12:]
         L.attn_varlen_block_m.restype = ctypes.c_int32
         L.attn_varlen_block_m.argtypes = [ctypes.c_int32]
+        L.attn_varlen_block_m_for.restype = ctypes.c_int32
+        L.attn_varlen_block_m_for.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        L.attn_varlen_one_stage_keys.restype = ctypes.c_int32
+        L.attn_varlen_one_stage_keys.argtypes = []
         L.attn_varlen_count_tiles.restype = ctypes.c_int64
         L.attn_varlen_count_tiles.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         L.attn_varlen_grid_plan.restype = ctypes.c_int32
-        L.attn_varlen_grid_plan.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _i64p, _i64p]
+        L.attn_varlen_grid_plan.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            _i64p, _i64p]
         L.attn_varlen_segments_per_launch.restype = ctypes.c_int32
         L.attn_varlen_segments_per_launch.argtypes = []
         L.attn_varlen_decode_tile.restype = ctypes.c_int32
@@ -162,10 +168,20 @@ def _cu_array(cu):
 
 # ---- host-only helpers (no GPU needed) -------------------------------------------------
 
-def block_m(head_dim: int) -> int:
-    r = lib().attn_varlen_block_m(head_dim)
+def block_m(head_dim: int, max_seqlen_k: int | None = None) -> int:
+    """Query rows per tile: of the general configuration, or, given the call's
+    max_seqlen_k, of the configuration the bf16 forward picks for it."""
+    if max_seqlen_k is None:
+        r = lib().attn_varlen_block_m(head_dim)
+    else:
+        r = lib().attn_varlen_block_m_for(head_dim, max_seqlen_k)
     _check(min(r, 0))
     return r
+
+
+def one_stage_keys() -> int:
+    """Longest key segment (max_seqlen_k) the one-stage configuration takes."""
+    return lib().attn_varlen_one_stage_keys()
 
 
 def count_tiles(cu_q, num_heads: int, block_m_: int) -> int:
@@ -176,10 +192,12 @@ def count_tiles(cu_q, num_heads: int, block_m_: int) -> int:
     return int(r)
 
 
-def grid_plan(cu_q, num_heads: int, head_dim: int):
+def grid_plan(cu_q, num_heads: int, head_dim: int, max_seqlen_k: int):
+    """(launches, workgroups) of attn_varlen_fwd for these cu_seqlens_q and max_seqlen_k."""
     arr, B = _cu_array(cu_q)
     nl, nw = ctypes.c_int64(), ctypes.c_int64()
-    _check(lib().attn_varlen_grid_plan(arr, B, num_heads, head_dim, ctypes.byref(nl), ctypes.byref(nw)))
+    _check(lib().attn_varlen_grid_plan(arr, B, num_heads, head_dim, max_seqlen_k, ctypes.byref(nl),
+                                       ctypes.byref(nw)))
     return nl.value, nw.value
 
 
@@ -301,9 +319,10 @@ def async_workspace_bytes(num_segments: int) -> int:
     return int(r)
 
 
-def async_grid(q_tokens: int, num_segments: int, num_heads: int, head_dim: int, max_seqlen_q: int) -> int:
+def async_grid(q_tokens: int, num_segments: int, num_heads: int, head_dim: int, max_seqlen_q: int,
+               max_seqlen_k: int) -> int:
     g = ctypes.c_int64()
-    _check(lib().attn_varlen_async_grid(q_tokens, num_segments, num_heads, head_dim, max_seqlen_q,
+    _check(lib().attn_varlen_async_grid(q_tokens, num_segments, num_heads, head_dim, max_seqlen_q, max_seqlen_k,
                                         ctypes.byref(g)))
     return g.value
 

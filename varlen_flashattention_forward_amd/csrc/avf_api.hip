@@ -200,12 +200,23 @@ int64_t fill_plan(AvfLaunchArgs& a, const int32_t* cu_q, const int32_t* cu_k, in
 // below 2^32 (HSA dispatch limit) with 256 threads per workgroup.
 constexpr int64_t kMaxTilesPerLaunch = (int64_t)1 << 23;
 
-// q8/k8/amax8: the 8-bit score operands (NULL for the bf16 path)
+// The bf16 forward takes the one-stage configuration when no key segment is
+// longer than one K/V stage (max_seqlen_k bounds every segment: checked
+// against cu_seqlens on the host, or by the device planner).
+bool use_one_stage(int32_t max_k, bool low_precision) {
+    return !low_precision && max_k <= avf_one_stage_keys();
+}
+
+int32_t fwd_block_m(int32_t D, bool one) { return one ? avf_block_m_one(D) : avf_block_m(D); }
+
+// max_k: the call's validated max_seqlen_k; q8/k8/amax8: the 8-bit score
+// operands (NULL for the bf16 path)
 int32_t run(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
             int32_t B, int32_t H, int32_t D, const attn_varlen_layout* st, float scale, void* out,
-            float* lse, hipStream_t stream, uint32_t flags, const SegStrides& seg,
+            float* lse, hipStream_t stream, uint32_t flags, int32_t max_k, const SegStrides& seg,
             const uint8_t* q8 = nullptr, const uint8_t* k8 = nullptr, const uint32_t* amax8 = nullptr) {
-    const int32_t bm = avf_block_m(D);
+    const bool one = use_one_stage(max_k, q8 != nullptr);
+    const int32_t bm = fwd_block_m(D, one);
     AvfLaunchArgs a;
     std::memset(&a, 0, sizeof a);
     a.q = q; a.k = k; a.v = v; a.o = out; a.lse = lse;
@@ -220,6 +231,7 @@ int32_t run(const void* q, const void* k, const void* v, const int32_t* cu_q, co
     a.causal = (flags & ATTN_VARLEN_CAUSAL) ? 1 : 0;
     a.q_seg = seg.q; a.k_seg = seg.k; a.v_seg = seg.v; a.o_seg = seg.o; a.lse_seg = seg.lse;
     a.q8 = q8; a.k8 = k8; a.amax8 = amax8;
+    a.one_stage = one ? 1 : 0;
     for (int32_t b0 = 0; b0 < B;) {
         // segments of this launch: at most AVF_SEGS_PER_LAUNCH and at most kMaxTilesPerLaunch tiles
         int32_t b1 = b0;
@@ -276,7 +288,7 @@ int32_t attn_varlen_fwd_hostcu_ex(const void* q, const void* k, const void* v, c
     rc = validate_all(q, k, v, cu_q, cu_k, B, H, D, max_q, max_k, st, scale, out, lse);
     if (rc != ATTN_VARLEN_OK || B == 0) return rc;
     return run(q, k, v, cu_q, cu_k, B, H, D, st, scale, out, lse, static_cast<hipStream_t>(stream), flags,
-               SegStrides{0, 0, 0, 0, 0});
+               max_k, SegStrides{0, 0, 0, 0, 0});
 }
 
 int32_t attn_varlen_fwd_hostcu(const void* q, const void* k, const void* v, const int32_t* cu_q,
@@ -305,7 +317,7 @@ int32_t attn_varlen_fwd_ex(const void* q, const void* k, const void* v, const in
     if (rc != ATTN_VARLEN_OK) return rc;
     rc = check_with_cu(cq, B, H, D, st, lse);
     if (rc != ATTN_VARLEN_OK) return rc;
-    return run(q, k, v, cq, ck, B, H, D, st, scale, out, lse, s, flags, SegStrides{0, 0, 0, 0, 0});
+    return run(q, k, v, cq, ck, B, H, D, st, scale, out, lse, s, flags, max_k, SegStrides{0, 0, 0, 0, 0});
 }
 
 int32_t attn_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_q_dev,
@@ -394,13 +406,22 @@ int32_t attn_fwd_batched(const void* q, const void* k, const void* v, int32_t W,
     const int32_t rc = batched_plan(q, k, v, W, Sq, Sk, H, D, bl, scale, flags, out, lse, &st, &seg, &cq, &ck);
     if (rc != ATTN_VARLEN_OK || W == 0 || Sq == 0) return rc;
     return run(q, k, v, cq.data(), ck.data(), W, H, D, &st, scale, out, lse, static_cast<hipStream_t>(stream),
-               flags, seg);
+               flags, Sk, seg);
 }
 
 int32_t attn_varlen_block_m(int32_t head_dim) {
     const int32_t bm = avf_block_m(head_dim);
     return bm > 0 ? bm : ATTN_VARLEN_EUNSUPPORTED;
 }
+
+int32_t attn_varlen_block_m_for(int32_t head_dim, int32_t max_seqlen_k) {
+    g_last_error.clear();
+    if (max_seqlen_k < 0) return fail(ATTN_VARLEN_EINVAL, "max_seqlen_k must be >= 0 (got %d)", max_seqlen_k);
+    const int32_t bm = fwd_block_m(head_dim, use_one_stage(max_seqlen_k, false));
+    return bm > 0 ? bm : ATTN_VARLEN_EUNSUPPORTED;
+}
+
+int32_t attn_varlen_one_stage_keys(void) { return avf_one_stage_keys(); }
 
 int64_t attn_varlen_count_tiles(const int32_t* cu_q, int32_t B, int32_t H, int32_t block_m) {
     g_last_error.clear();
@@ -414,11 +435,12 @@ int64_t attn_varlen_count_tiles(const int32_t* cu_q, int32_t B, int32_t H, int32
 
 int32_t attn_varlen_segments_per_launch(void) { return AVF_SEGS_PER_LAUNCH; }
 
-int32_t attn_varlen_grid_plan(const int32_t* cu_q, int32_t B, int32_t H, int32_t D,
+int32_t attn_varlen_grid_plan(const int32_t* cu_q, int32_t B, int32_t H, int32_t D, int32_t max_k,
                               int64_t* launches, int64_t* workgroups) {
     g_last_error.clear();
     if (!cu_q || !launches || !workgroups) return fail(ATTN_VARLEN_ENULL, "NULL argument");
-    const int32_t bm = avf_block_m(D);
+    if (max_k < 0) return fail(ATTN_VARLEN_EINVAL, "max_seqlen_k must be >= 0 (got %d)", max_k);
+    const int32_t bm = fwd_block_m(D, use_one_stage(max_k, false));
     if (bm <= 0) return fail(ATTN_VARLEN_EUNSUPPORTED, "head_dim %d not supported", D);
     if (B < 0 || H <= 0) return fail(ATTN_VARLEN_EINVAL, "bad counts");
     int64_t nl = 0, nw = 0;
@@ -779,13 +801,13 @@ int64_t attn_varlen_async_workspace_bytes(int32_t B) {
     return async_workspace_bytes(B);
 }
 
-int32_t attn_varlen_async_grid(int64_t q_tokens, int32_t B, int32_t H, int32_t D, int32_t max_q,
+int32_t attn_varlen_async_grid(int64_t q_tokens, int32_t B, int32_t H, int32_t D, int32_t max_q, int32_t max_k,
                                int64_t* workgroups) {
     g_last_error.clear();
     if (!workgroups) return fail(ATTN_VARLEN_ENULL, "NULL argument");
-    const int32_t bm = avf_block_m(D);
+    if (B < 0 || H <= 0 || q_tokens < 0 || max_q < 0 || max_k < 0) return fail(ATTN_VARLEN_EINVAL, "bad counts");
+    const int32_t bm = fwd_block_m(D, use_one_stage(max_k, false));
     if (bm <= 0) return fail(ATTN_VARLEN_EUNSUPPORTED, "head_dim %d not supported", D);
-    if (B < 0 || H <= 0 || q_tokens < 0 || max_q < 0) return fail(ATTN_VARLEN_EINVAL, "bad counts");
     *workgroups = async_grid(async_tile_bound(q_tokens, B, H, bm, max_q));
     return ATTN_VARLEN_OK;
 }
@@ -812,7 +834,9 @@ int32_t attn_varlen_fwd_async(const void* q, const void* k, const void* v, const
     if (lse && H > 1 && st->lse_head != 0 && st->lse_head < st->q_tokens)
         return fail(ATTN_VARLEN_EINVAL, "lse_head %lld is smaller than q_tokens %lld", (long long)st->lse_head,
                     (long long)st->q_tokens);
-    const int32_t bm = avf_block_m(D);
+    // the planner rejects any segment over max_k, so max_k may pick the one-stage configuration
+    const bool one = use_one_stage(max_k, false);
+    const int32_t bm = fwd_block_m(D, one);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t* ws = static_cast<int32_t*>(workspace);
     hipError_t e = avf_plan_launch(cu_q_dev, cu_k_dev, B, H, bm, 0, max_q, max_k, st->q_tokens, st->k_tokens, ws, s);
@@ -836,6 +860,7 @@ int32_t attn_varlen_fwd_async(const void* q, const void* k, const void* v, const
     a.cu_k = cu_k_dev;
     a.num_segs = B;
     a.num_tiles = (int32_t)grid;
+    a.one_stage = one ? 1 : 0;
     e = avf_launch(a, D, s);
     if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ATTN_VARLEN_OK;
@@ -894,7 +919,8 @@ int32_t fp8_run(const void* q, const void* k, const void* v, const int32_t* cu_q
     qa.k8 = reinterpret_cast<uint8_t*>(ws + l.k8);
     const hipError_t e = avf_fp8_quantize(qa, s);
     if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "quantization launch failed: %s", hipGetErrorString(e));
-    return run(q, k, v, cu_q, cu_k, B, H, D, st, scale, out, lse, s, flags, SegStrides{0, 0, 0, 0, 0}, qa.q8, qa.k8,
+    return run(q, k, v, cu_q, cu_k, B, H, D, st, scale, out, lse, s, flags, INT32_MAX, SegStrides{0, 0, 0, 0, 0},
+               qa.q8, qa.k8,
                qa.amax);
 }
 

@@ -78,8 +78,9 @@ __device__ constexpr int k8_swz(int key) {
 
 // LDS holds a ring of KBUF K stages followed by a ring of VBUF V stages. V
 // lives one stage longer than K because each wave's P.V product trails its
-// Q.K^T product by one 32-key sub-block, across stage boundaries.
-template <int D, int QB, int NW, int BN, bool F8 = false>
+// Q.K^T product by one 32-key sub-block, across stage boundaries. ONE: every
+// segment has at most BN keys, so a tile has one stage and one buffer each.
+template <int D, int QB, int NW, int BN, bool F8 = false, bool ONE = false>
 struct Tile {
     static constexpr int NT = NW * 64;          // threads per workgroup
     static constexpr int BM = QB * 32 * NW;     // query rows per tile
@@ -88,7 +89,7 @@ struct Tile {
     static constexpr int KB = BN / 32;          // 32-key sub-blocks per K/V stage
     static constexpr int ROWB = D * 2;          // bytes per K/V row in LDS
     static constexpr int SBYTES = BN * ROWB;    // one stage of K (or of V)
-    static constexpr int KBUF = 2, VBUF = 3;
+    static constexpr int KBUF = ONE ? 1 : 2, VBUF = ONE ? 1 : 3;
     // K stages hold bf16 rows, or with F8 the E4M3 codes (D bytes per row)
     static constexpr int KROWB = F8 ? D : 2 * D;
     static constexpr int KSBYTES = BN * KROWB;
@@ -112,9 +113,13 @@ struct Tile {
 // tiles and leaves the loop at the plan's real tile count (below).
 // F8 (compile-time): S^T = K Q^T from per-head E4M3 codes of q and k with the
 // depth-64 8-bit MFMA (v_mfma_f32_32x32x64_f8f6f4); P.V stays bf16.
-template <int D, int QB, int NW, int BN, bool CAUSAL, bool DEVPLAN, bool F8>
-__global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs a) {
-    using T = Tile<D, QB, NW, BN, F8>;
+// ONE (compile-time): every segment of the call has at most BN keys (the host
+// checked max_seqlen_k against cu_seqlens, or the device planner does): one
+// K/V stage per tile, LDS for one stage only, so that two workgroups of NW
+// waves share a CU and one's loads overlap the other's arithmetic.
+template <int D, int QB, int NW, int BN, bool CAUSAL, bool DEVPLAN, bool F8, bool ONE>
+__global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunchArgs a) {
+    using T = Tile<D, QB, NW, BN, F8, ONE>;
     constexpr int BM = T::BM;
     __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
     // LDS byte address of the array (M0 operand of the direct loads)
@@ -133,6 +138,9 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
                         const int32_t qs1, const int32_t ks0, const int32_t ks1) {
     const int32_t lq = qs1 - qs0;
     const int32_t lk = ks1 - ks0;
+    // a one-stage tile has LDS for BN keys only (never reached: the host and
+    // the device planner reject longer segments before choosing it)
+    if (ONE && lk > BN) return;
     // Causal: later query blocks see more keys, so they are dispatched first
     // (the block order within a (segment, head) is reversed).
     const int32_t mblk = CAUSAL ? (lq + BM - 1) / BM - 1 - tile_mblk : tile_mblk;
@@ -623,7 +631,7 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
 
     if (nkt > 0) {
         load_stage(0, 0, 0);
-        if (nkt > 1) load_stage(1, 1, 1);
+        if (!ONE && nkt > 1) load_stage(1, 1, 1);
         // Wait for everything issued so far (Q fragments and the first two
         // stages), once per tile: the compiler does not see the stage loads,
         // so only a full vmcnt(0) tells it that the Q fragments have landed;
@@ -671,14 +679,14 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
             vbuf = vbuf == 2 ? 0 : vbuf + 1;
         };
         // stages every row sees whole, then the ones crossing the causal diagonal
-        const int32_t nfree = min(jmask, nkt - 1);
+        const int32_t nfree = ONE ? 0 : min(jmask, nkt - 1);
         int32_t j = 0;
         for (; j < nfree; ++j) {
             stage(j, kbuf, vnext, kbuf ? -T::KSBYTES : T::KSBYTES, (vbuf - vprev) * T::SBYTES, std::false_type{},
                   std::false_type{});
             advance();
         }
-        if constexpr (CAUSAL) {
+        if constexpr (CAUSAL && !ONE) {
             for (; j + 1 < nkt; ++j) {
                 stage(j, kbuf, vnext, kbuf ? -T::KSBYTES : T::KSBYTES, (vbuf - vprev) * T::SBYTES, std::false_type{},
                       std::true_type{});
@@ -744,16 +752,17 @@ __global__ void __launch_bounds__(NW * 64, 1) avf_fwd_kernel(const AvfLaunchArgs
     }
 }
 
-template <int D, int QB, int NW, int BN>
+template <int D, int QB, int NW, int BN, bool ONE>
 hipError_t launch_cfg(const AvfLaunchArgs& a, hipStream_t stream) {
     // grid: the exact tile count, or with a device plan the host's bound
     const dim3 grid((uint32_t)a.num_tiles), block(NW * 64);
     if (a.q8) {
-        if constexpr (D % 64 == 0) {
+        if constexpr (D % 64 == 0 && !ONE) {
             if (a.causal)
-                hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true, false, true>), grid, block, 0, stream, a);
+                hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true, false, true, false>), grid, block, 0, stream, a);
             else
-                hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false, false, true>), grid, block, 0, stream, a);
+                hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false, false, true, false>), grid, block, 0, stream,
+                                   a);
             return hipGetLastError();
         } else {
             return hipErrorInvalidValue;
@@ -761,14 +770,14 @@ hipError_t launch_cfg(const AvfLaunchArgs& a, hipStream_t stream) {
     }
     if (a.dev_plan) {
         if (a.causal)
-            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true, true, false>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true, true, false, ONE>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false, true, false>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false, true, false, ONE>), grid, block, 0, stream, a);
     } else {
         if (a.causal)
-            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true, false, false>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true, false, false, ONE>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false, false, false>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, false, false, false, ONE>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }
@@ -795,6 +804,17 @@ template <> struct Cfg<128> : CfgOf<AVF_CFG_D128> {};
 template <int D>
 constexpr int block_m_of() { return Cfg<D>::QB * 32 * Cfg<D>::NW; }
 
+// One-stage configuration (segments of at most kOneStageKeys keys): 4 waves,
+// 128 query rows, one 128-key K/V stage; two workgroups per CU.
+constexpr int kOneNW = 4, kOneStageKeys = 128;
+constexpr int kOneBlockM = 32 * kOneNW;
+
+template <int D>
+hipError_t launch_d(const AvfLaunchArgs& a, hipStream_t stream) {
+    if (a.one_stage) return launch_cfg<D, 1, kOneNW, kOneStageKeys, true>(a, stream);
+    return launch_cfg<D, Cfg<D>::QB, Cfg<D>::NW, Cfg<D>::BN, false>(a, stream);
+}
+
 }  // namespace
 
 int32_t avf_block_m(int32_t head_dim) {
@@ -806,11 +826,17 @@ int32_t avf_block_m(int32_t head_dim) {
     }
 }
 
+int32_t avf_block_m_one(int32_t head_dim) {
+    return (head_dim == 64 || head_dim == 96 || head_dim == 128) ? kOneBlockM : -1;
+}
+
+int32_t avf_one_stage_keys() { return kOneStageKeys; }
+
 hipError_t avf_launch(const AvfLaunchArgs& a, int32_t head_dim, hipStream_t stream) {
     switch (head_dim) {
-        case 64: return launch_cfg<64, Cfg<64>::QB, Cfg<64>::NW, Cfg<64>::BN>(a, stream);
-        case 96: return launch_cfg<96, Cfg<96>::QB, Cfg<96>::NW, Cfg<96>::BN>(a, stream);
-        case 128: return launch_cfg<128, Cfg<128>::QB, Cfg<128>::NW, Cfg<128>::BN>(a, stream);
+        case 64: return launch_d<64>(a, stream);
+        case 96: return launch_d<96>(a, stream);
+        case 128: return launch_d<128>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

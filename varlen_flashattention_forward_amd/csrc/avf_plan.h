@@ -29,6 +29,8 @@ struct AvfLaunchArgs {
     int64_t q_seg, k_seg, v_seg, o_seg, lse_seg;
     int32_t seg0;       // global index of this launch's first segment
     int32_t causal;     // 1: query row r of a segment sees keys j <= r + Lk - Lq
+    int32_t one_stage;  // 1: every segment has at most avf_one_stage_keys() keys (checked by
+                        // the caller): the one-stage configuration, block_m avf_block_m_one
     // Device plan (sync-free entry): the planner's workspace (status, tile
     // count, tile prefix of all num_segs segments) and the caller's device
     // cu_seqlens; NULL for a host-planned launch, which uses the arrays below.
@@ -115,4 +117,9 @@ hipError_t avf_launch(const AvfLaunchArgs& args, int32_t head_dim, hipStream_t s
 hipError_t avf_plan_launch(const int32_t* cu_q, const int32_t* cu_k, int32_t num_segs, int32_t num_heads,
                            int32_t block, int32_t tiled, int32_t max_q, int32_t max_k, int64_t q_tokens,
                            int64_t k_tokens, int32_t* workspace, hipStream_t stream);
+// Query rows per tile of the general configuration and of the one-stage
+// configuration (segments of at most avf_one_stage_keys() keys); -1 for an
+// unsupported head_dim.
 int32_t avf_block_m(int32_t head_dim);
+int32_t avf_block_m_one(int32_t head_dim);
+int32_t avf_one_stage_keys();

@@ -22,6 +22,11 @@ the pages' workloads are a private video model and a private training job):
 * ``causal_77k``: ``dense_77k`` with the causal mask (query row r of a segment
   sees keys j <= r + Lk - Lq); the pages only run causal=False, so this is an
   extension, with FLOPs counted over the visible (query, key) pairs.
+* ``short_128``, ``short_256``, ``short_512``: 64 segments of S = 128, 256,
+  512 tokens, H=56, D=128, N(0,1)*0.1: the short-segment regime, where the
+  arithmetic intensity falls below the MFMA/HBM ridge and the forward is
+  measured in HBM GB/s; shorter than the W x S sweep (S = 1024 .. 24576) of
+  the FA4 SM120 issue page ("What rules things out").
 * ``bwd_9728``: the backward case of the _bwd_preprocess page ("Verified
   sample", repro script): N=410923 in segments [0,225304,410923], H=16, D=96;
   q, k, v one contiguous randn(3, N, H, D)*0.1 draw, dout (``make_dout``) an
@@ -118,6 +123,9 @@ WORKLOADS = {
                              0.1, True, layout="stride9728", outer_stride=9728),
     "dense_117k": Workload("dense_117k", 56, 128, (0, 117000), (0, 117000), 1.0, True),
     "causal_77k": Workload("causal_77k", 56, 128, (0, 77000), (0, 77000), 1.0, True, causal=True),
+    "short_128": Workload("short_128", 56, 128, _cu_uniform(64, 128), _cu_uniform(64, 128), 0.1, True),
+    "short_256": Workload("short_256", 56, 128, _cu_uniform(64, 256), _cu_uniform(64, 256), 0.1, True),
+    "short_512": Workload("short_512", 56, 128, _cu_uniform(64, 512), _cu_uniform(64, 512), 0.1, True),
     # backward: contiguous q, k, v; dout an [N, H, D] view of an [N, 9728] buffer (make_dout)
     "bwd_9728": Workload("bwd_9728", 16, 96, (0, 225304, 410923), (0, 225304, 410923), 0.1, True,
                          outer_stride=9728),
