@@ -90,6 +90,30 @@ def test_sync_free_many_segments_one_launch():
     assert torch.equal(a_o, b_o) and torch.equal(a_l[:, :w.total_q], b_l[:, :w.total_q])
 
 
+@pytest.mark.parametrize("B", [1, 63, 64, 65, 4097, 5000])
+def test_sync_free_segment_search_boundaries(B):
+    """Segment counts at the steps of the device decode's 64-way search (one
+    step up to 64 segments, two up to 4096, three beyond), with empty segments
+    in long runs so that equal prefix entries straddle probe positions."""
+    announce(f"sync-free segment search B={B}")
+    rng = np.random.default_rng(100 + B)
+    lens_q = rng.integers(1, 40, B)
+    lens_k = rng.integers(1, 40, B)
+    for a in rng.integers(0, B, max(1, B // 50)):  # runs of empty query segments
+        lens_q[a:a + int(rng.integers(1, 200))] = 0
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(int).tolist()
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(int).tolist()
+    if cu_q[-1] == 0:
+        cu_q[-1] = 1  # at least one row: make the last segment one row long
+    w = custom(f"search{B}", 2, 64, cu_q, cu_k, std=1.0)
+    t = make_inputs(w, "cuda", seed=7)
+    a_o, a_l = host_planned(t, w)
+    b_o, b_l, ws = sync_free(t, w)
+    torch.cuda.synchronize()
+    assert avf.async_status(ws) == 0
+    assert torch.equal(a_o, b_o) and torch.equal(a_l[:, :w.total_q], b_l[:, :w.total_q])
+
+
 def test_sync_free_grid_smaller_than_tile_count_loops():
     """More tiles than the 8192-workgroup cap: workgroups take several tiles."""
     announce("sync-free looping grid")

@@ -76,6 +76,40 @@ __device__ constexpr int k8_swz(int key) {
     return D == 128 ? (key >> 1) & 7 : (key >> 2) & 3;
 }
 
+// Device-plan tile decode: segment = the largest s with tile_start[s] <=
+// linear (empty segments repeat their successor's start and are never
+// chosen), found by a 64-way search. Each lane probes one prefix entry per
+// step and a ballot picks the last probe at or below `linear`, so a step
+// costs one global round trip and shrinks the candidates 64-fold (one step
+// for up to 64 segments) where a binary search pays one round trip per
+// halving. Every probe index stays below num_segs; every wave of the
+// workgroup computes the same result.
+__device__ inline AvfTile decode_wave(int32_t linear, const int32_t* tile_start, const int32_t* cu_q,
+                                      int32_t num_segs, int32_t block_m, int lane) {
+    int32_t lo = 0, n = num_segs;  // candidates [lo, lo + n); tile_start[lo] <= linear
+    int32_t start = 0;             // tile_start[lo]
+    for (;;) {
+        const int32_t stride = n > 64 ? (n + 63) / 64 : 1;
+        const int32_t off = lane * stride;
+        const bool probe = off < n;
+        const int32_t v = probe ? tile_start[lo + off] : INT32_MAX;
+        const uint64_t below = __ballot(probe && v <= linear);  // bit 0 always set
+        const int last = 63 - __clzll((long long)below);
+        start = __shfl(v, last);
+        lo += last * stride;
+        if (stride == 1) break;
+        n = min(stride, n - last * stride);
+    }
+    const int32_t lq = cu_q[lo + 1] - cu_q[lo];
+    const int32_t mtiles = (lq + block_m - 1) / block_m;
+    const int32_t r = linear - start;
+    AvfTile t;
+    t.seg = lo;
+    t.head = r / mtiles;
+    t.mblk = r - t.head * mtiles;
+    return t;
+}
+
 // LDS holds a ring of KBUF K stages followed by a ring of VBUF V stages. V
 // lives one stage longer than K because each wave's P.V product trails its
 // Q.K^T product by one 32-key sub-block, across stage boundaries. ONE: every
@@ -126,10 +160,10 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
     const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
+    int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31;
-    const int hf = lane >> 5;
+    int l32 = lane & 31;
+    int hf = lane >> 5;
 
     // One tile: query block tile_mblk (in dispatch order) of head h of the
     // launch's segment seg, whose query rows are [qs0, qs1) and key rows
@@ -742,8 +776,24 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
         if (plan[0] != 0) return;
         const int32_t nt = plan[1];
         for (int32_t idx = (int32_t)blockIdx.x; idx < nt; idx += (int32_t)gridDim.x) {
+            // The lane indices are made opaque to the optimizer once per tile,
+            // so the per-lane LDS and buffer offsets derived from them are
+            // recomputed for each tile (a few VALU instructions) instead of
+            // being kept live across tiles, where they spill (D = 128: 52
+            // spill accesses, 19 of them in the stage loop, against 6 and 3).
+            // The causal instantiations spill more with it and keep the
+            // hoisted offsets.
+            if constexpr (!CAUSAL) {
+                pin(lane);
+                pin(l32);
+                pin(hf);
+            }
             const int32_t linear = avf_linear_tile(idx, nt);
-            const AvfTile tile = avf_decode(linear, plan + AVF_PLAN_HEADER_WORDS, a.cu_q, a.num_segs, a.num_heads, BM);
+            // (the causal instantiations keep the binary search: with the
+            // 64-way search their stage loop measured 16% slower)
+            const AvfTile tile =
+                CAUSAL ? avf_decode(linear, plan + AVF_PLAN_HEADER_WORDS, a.cu_q, a.num_segs, a.num_heads, BM)
+                       : decode_wave(linear, plan + AVF_PLAN_HEADER_WORDS, a.cu_q, a.num_segs, BM, lane);
             run_tile(tile.seg, tile.mblk, tile.head, a.cu_q[tile.seg], a.cu_q[tile.seg + 1], a.cu_k[tile.seg],
                      a.cu_k[tile.seg + 1]);
             // the next tile's first loads overwrite LDS buffers this one read
