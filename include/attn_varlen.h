@@ -135,19 +135,24 @@ int32_t attn_varlen_block_m(int32_t head_dim);
 
 /*
  * Query rows per tile the bf16 forward uses for a call with this
- * max_seqlen_k. When no key segment can be longer than one K/V stage
- * (max_seqlen_k <= attn_varlen_one_stage_keys(), 128), a tile needs LDS for
- * one stage only, and the forward switches to smaller workgroups that share a
- * CU in pairs. That is the short-segment, HBM-bound regime: with one segment
- * of keys per tile there is no K/V reuse to pipeline. The choice follows the
- * caller's max_seqlen_k, which every entry point validates against the
- * segments (on the host, or in the device planner), so it never depends on
- * values the host cannot see. The 8-bit forward always uses the general
- * configuration. Returns ATTN_VARLEN_EUNSUPPORTED for an unsupported
- * head_dim and ATTN_VARLEN_EINVAL for max_seqlen_k < 0.
+ * max_seqlen_k. Short key segments are the HBM-bound regime, where a tile
+ * has little K/V to stream, so the forward switches to smaller workgroups
+ * (128 query rows) that share a CU in pairs and overlap each other's loads:
+ *   max_seqlen_k <= attn_varlen_one_stage_keys() (128): one K/V stage per
+ *     tile, LDS for that stage only;
+ *   max_seqlen_k <= attn_varlen_short_stage_keys() (512): 64-key stages in
+ *     smaller LDS rings;
+ *   longer: the general configuration, attn_varlen_block_m(head_dim).
+ * All three give bit-identical results. The choice follows the caller's
+ * max_seqlen_k, which every entry point validates against the segments (on
+ * the host, or in the device planner), so it never depends on values the host
+ * cannot see. The 8-bit forward always uses the general configuration.
+ * Returns ATTN_VARLEN_EUNSUPPORTED for an unsupported head_dim and
+ * ATTN_VARLEN_EINVAL for max_seqlen_k < 0.
  */
 int32_t attn_varlen_block_m_for(int32_t head_dim, int32_t max_seqlen_k);
 int32_t attn_varlen_one_stage_keys(void);
+int32_t attn_varlen_short_stage_keys(void);
 
 /*
  * Exact tile count H * sum_b ceil(Lq_b / block_m) for host cu_seqlens_q

@@ -86,7 +86,7 @@ def test_our_grid_is_exact_for_every_workload():
     for w in WORKLOADS.values():
         bm = avf.block_m(w.head_dim, w.max_seqlen_k)
         # segments of at most one K/V stage take the one-stage configuration (128-row tiles)
-        assert bm == (128 if w.max_seqlen_k <= avf.one_stage_keys() else avf.block_m(w.head_dim))
+        assert bm == (128 if w.max_seqlen_k <= avf.short_stage_keys() else avf.block_m(w.head_dim))
         exact = w.num_heads * sum(math.ceil((b - a) / bm) for a, b in zip(w.cu_q[:-1], w.cu_q[1:]))
         launches, wgs = avf.grid_plan(w.cu_q, w.num_heads, w.head_dim, w.max_seqlen_k)
         assert wgs == exact == avf.count_tiles(w.cu_q, w.num_heads, bm)
@@ -100,10 +100,10 @@ def test_grid_plan_splits_long_segment_lists():
     cu = [0]
     for x in lens:
         cu.append(cu[-1] + x)
-    for max_k in (max(lens), 128):
+    for max_k in (max(lens), 512, 128):
         launches, wgs = avf.grid_plan(cu, 3, 128, max_k)
         bm = avf.block_m(128, max_k)
-        assert bm == (avf.block_m(128) if max_k > 128 else 128)
+        assert bm == (avf.block_m(128) if max_k > 512 else 128)
         assert wgs == 3 * sum(math.ceil(x / bm) for x in lens)
         assert launches == math.ceil(len(lens) / spl)
 
@@ -211,13 +211,14 @@ def test_validate_never_needs_lse_head_with_one_head():
 
 
 def test_block_m_and_unsupported_dims():
-    assert avf.one_stage_keys() == 128
+    assert avf.one_stage_keys() == 128 and avf.short_stage_keys() == 512
     for d in (64, 96, 128):
         bm = avf.block_m(d)
         assert bm > 0 and bm % 32 == 0
         # max_seqlen_k picks the configuration: one stage up to 128 keys
         assert avf.block_m(d, 0) == avf.block_m(d, 1) == avf.block_m(d, 128) == 128
-        assert avf.block_m(d, 129) == avf.block_m(d, 1 << 30) == bm
+        assert avf.block_m(d, 129) == avf.block_m(d, 512) == 128
+        assert avf.block_m(d, 513) == avf.block_m(d, 1 << 30) == bm
         with pytest.raises(avf.AttnVarlenError, match="EINVAL"):
             avf.block_m(d, -1)
     with pytest.raises(avf.AttnVarlenError):

@@ -30,7 +30,7 @@ EXPORTED_SYMBOLS = (
     "attn_varlen_bwd_grid_plan", "attn_varlen_async_workspace_bytes", "attn_varlen_fwd_async",
     "attn_varlen_async_status", "attn_varlen_async_grid", "attn_varlen_fp8_workspace_bytes",
     "attn_varlen_fp8_workspace_offsets", "attn_varlen_fwd_fp8", "attn_varlen_fwd_fp8_hostcu",
-    "attn_varlen_block_m_for", "attn_varlen_one_stage_keys",
+    "attn_varlen_block_m_for", "attn_varlen_one_stage_keys", "attn_varlen_short_stage_keys",
 )
 
 CAUSAL = 1  # ATTN_VARLEN_CAUSAL
@@ -134,6 +134,8 @@ def lib():
         L.attn_varlen_block_m_for.argtypes = [ctypes.c_int32, ctypes.c_int32]
         L.attn_varlen_one_stage_keys.restype = ctypes.c_int32
         L.attn_varlen_one_stage_keys.argtypes = []
+        L.attn_varlen_short_stage_keys.restype = ctypes.c_int32
+        L.attn_varlen_short_stage_keys.argtypes = []
         L.attn_varlen_count_tiles.restype = ctypes.c_int64
         L.attn_varlen_count_tiles.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         L.attn_varlen_grid_plan.restype = ctypes.c_int32
@@ -182,6 +184,11 @@ def block_m(head_dim: int, max_seqlen_k: int | None = None) -> int:
 def one_stage_keys() -> int:
     """Longest key segment (max_seqlen_k) the one-stage configuration takes."""
     return lib().attn_varlen_one_stage_keys()
+
+
+def short_stage_keys() -> int:
+    """Longest key segment (max_seqlen_k) the 64-key-stage configuration takes."""
+    return lib().attn_varlen_short_stage_keys()
 
 
 def count_tiles(cu_q, num_heads: int, block_m_: int) -> int:

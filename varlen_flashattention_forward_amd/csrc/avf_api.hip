@@ -200,14 +200,21 @@ int64_t fill_plan(AvfLaunchArgs& a, const int32_t* cu_q, const int32_t* cu_k, in
 // below 2^32 (HSA dispatch limit) with 256 threads per workgroup.
 constexpr int64_t kMaxTilesPerLaunch = (int64_t)1 << 23;
 
-// The bf16 forward takes the one-stage configuration when no key segment is
-// longer than one K/V stage (max_seqlen_k bounds every segment: checked
-// against cu_seqlens on the host, or by the device planner).
-bool use_one_stage(int32_t max_k, bool low_precision) {
-    return !low_precision && max_k <= avf_one_stage_keys();
+// Forward configuration from the call's max_seqlen_k (which bounds every key
+// segment: checked against cu_seqlens on the host, or by the device planner):
+// one-stage (one 128-key K/V stage), short-stage (64-key stages), or the
+// general one. Both small ones run 4-wave, 128-row workgroups two per CU; the
+// 8-bit forward always takes the general configuration.
+enum class FwdCfg { general, one_stage, short_stage };
+
+FwdCfg fwd_config(int32_t max_k, bool low_precision) {
+    if (low_precision) return FwdCfg::general;
+    if (max_k <= avf_one_stage_keys()) return FwdCfg::one_stage;
+    if (max_k <= avf_short_stage_keys()) return FwdCfg::short_stage;
+    return FwdCfg::general;
 }
 
-int32_t fwd_block_m(int32_t D, bool one) { return one ? avf_block_m_one(D) : avf_block_m(D); }
+int32_t fwd_block_m(int32_t D, FwdCfg c) { return c == FwdCfg::general ? avf_block_m(D) : avf_block_m_one(D); }
 
 // max_k: the call's validated max_seqlen_k; q8/k8/amax8: the 8-bit score
 // operands (NULL for the bf16 path)
@@ -215,8 +222,8 @@ int32_t run(const void* q, const void* k, const void* v, const int32_t* cu_q, co
             int32_t B, int32_t H, int32_t D, const attn_varlen_layout* st, float scale, void* out,
             float* lse, hipStream_t stream, uint32_t flags, int32_t max_k, const SegStrides& seg,
             const uint8_t* q8 = nullptr, const uint8_t* k8 = nullptr, const uint32_t* amax8 = nullptr) {
-    const bool one = use_one_stage(max_k, q8 != nullptr);
-    const int32_t bm = fwd_block_m(D, one);
+    const FwdCfg cfg = fwd_config(max_k, q8 != nullptr);
+    const int32_t bm = fwd_block_m(D, cfg);
     AvfLaunchArgs a;
     std::memset(&a, 0, sizeof a);
     a.q = q; a.k = k; a.v = v; a.o = out; a.lse = lse;
@@ -231,7 +238,8 @@ int32_t run(const void* q, const void* k, const void* v, const int32_t* cu_q, co
     a.causal = (flags & ATTN_VARLEN_CAUSAL) ? 1 : 0;
     a.q_seg = seg.q; a.k_seg = seg.k; a.v_seg = seg.v; a.o_seg = seg.o; a.lse_seg = seg.lse;
     a.q8 = q8; a.k8 = k8; a.amax8 = amax8;
-    a.one_stage = one ? 1 : 0;
+    a.one_stage = cfg == FwdCfg::one_stage;
+    a.short_stage = cfg == FwdCfg::short_stage;
     for (int32_t b0 = 0; b0 < B;) {
         // segments of this launch: at most AVF_SEGS_PER_LAUNCH and at most kMaxTilesPerLaunch tiles
         int32_t b1 = b0;
@@ -417,11 +425,13 @@ int32_t attn_varlen_block_m(int32_t head_dim) {
 int32_t attn_varlen_block_m_for(int32_t head_dim, int32_t max_seqlen_k) {
     g_last_error.clear();
     if (max_seqlen_k < 0) return fail(ATTN_VARLEN_EINVAL, "max_seqlen_k must be >= 0 (got %d)", max_seqlen_k);
-    const int32_t bm = fwd_block_m(head_dim, use_one_stage(max_seqlen_k, false));
+    const int32_t bm = fwd_block_m(head_dim, fwd_config(max_seqlen_k, false));
     return bm > 0 ? bm : ATTN_VARLEN_EUNSUPPORTED;
 }
 
 int32_t attn_varlen_one_stage_keys(void) { return avf_one_stage_keys(); }
+
+int32_t attn_varlen_short_stage_keys(void) { return avf_short_stage_keys(); }
 
 int64_t attn_varlen_count_tiles(const int32_t* cu_q, int32_t B, int32_t H, int32_t block_m) {
     g_last_error.clear();
@@ -440,7 +450,7 @@ int32_t attn_varlen_grid_plan(const int32_t* cu_q, int32_t B, int32_t H, int32_t
     g_last_error.clear();
     if (!cu_q || !launches || !workgroups) return fail(ATTN_VARLEN_ENULL, "NULL argument");
     if (max_k < 0) return fail(ATTN_VARLEN_EINVAL, "max_seqlen_k must be >= 0 (got %d)", max_k);
-    const int32_t bm = fwd_block_m(D, use_one_stage(max_k, false));
+    const int32_t bm = fwd_block_m(D, fwd_config(max_k, false));
     if (bm <= 0) return fail(ATTN_VARLEN_EUNSUPPORTED, "head_dim %d not supported", D);
     if (B < 0 || H <= 0) return fail(ATTN_VARLEN_EINVAL, "bad counts");
     int64_t nl = 0, nw = 0;
@@ -806,7 +816,7 @@ int32_t attn_varlen_async_grid(int64_t q_tokens, int32_t B, int32_t H, int32_t D
     g_last_error.clear();
     if (!workgroups) return fail(ATTN_VARLEN_ENULL, "NULL argument");
     if (B < 0 || H <= 0 || q_tokens < 0 || max_q < 0 || max_k < 0) return fail(ATTN_VARLEN_EINVAL, "bad counts");
-    const int32_t bm = fwd_block_m(D, use_one_stage(max_k, false));
+    const int32_t bm = fwd_block_m(D, fwd_config(max_k, false));
     if (bm <= 0) return fail(ATTN_VARLEN_EUNSUPPORTED, "head_dim %d not supported", D);
     *workgroups = async_grid(async_tile_bound(q_tokens, B, H, bm, max_q));
     return ATTN_VARLEN_OK;
@@ -835,8 +845,8 @@ int32_t attn_varlen_fwd_async(const void* q, const void* k, const void* v, const
         return fail(ATTN_VARLEN_EINVAL, "lse_head %lld is smaller than q_tokens %lld", (long long)st->lse_head,
                     (long long)st->q_tokens);
     // the planner rejects any segment over max_k, so max_k may pick the one-stage configuration
-    const bool one = use_one_stage(max_k, false);
-    const int32_t bm = fwd_block_m(D, one);
+    const FwdCfg cfg = fwd_config(max_k, false);
+    const int32_t bm = fwd_block_m(D, cfg);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t* ws = static_cast<int32_t*>(workspace);
     hipError_t e = avf_plan_launch(cu_q_dev, cu_k_dev, B, H, bm, 0, max_q, max_k, st->q_tokens, st->k_tokens, ws, s);
@@ -860,7 +870,8 @@ int32_t attn_varlen_fwd_async(const void* q, const void* k, const void* v, const
     a.cu_k = cu_k_dev;
     a.num_segs = B;
     a.num_tiles = (int32_t)grid;
-    a.one_stage = one ? 1 : 0;
+    a.one_stage = cfg == FwdCfg::one_stage;
+    a.short_stage = cfg == FwdCfg::short_stage;
     e = avf_launch(a, D, s);
     if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ATTN_VARLEN_OK;

@@ -134,7 +134,11 @@ struct Tile {
     static constexpr int NIW = NI / NW;         // ... per wave
     static constexpr int LPS = 2 * NIW;         // direct loads per wave and stage (K and V)
     static_assert(D % 32 == 0 && BN % 32 == 0 && SBYTES % 1024 == 0, "tile shape");
-    static_assert(KB >= 4 && KB % 2 == 0, "four or more sub-blocks per stage, parity repeating every stage");
+    static_assert(KB >= 2 && KB % 2 == 0, "an even number of sub-blocks per stage (parity repeats every stage)");
+    // Two sub-blocks per stage: the barrier sits at sub-block 0, where V of
+    // the previous stage is still being read, so V stages load one stage
+    // behind K (see `stage`).
+    static constexpr bool VLAG = KB == 2;
     static_assert(NI % NW == 0, "every wave issues the same number of loads per stage");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS rings");
     static_assert(!F8 || (D % 64 == 0 && NIK % NW == 0), "8-bit K stages: depth-64 steps, whole loads per wave");
@@ -259,7 +263,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
     const int32_t jmask = kfull / BN;  // first stage that needs the per-row causal mask
     const uint32_t k_rs = (uint32_t)(a.k_row * 2);
     const uint32_t v_rs = (uint32_t)(a.v_row * 2);
-    auto load_stage = [&](int32_t j, int kbuf, int vbuf) {
+    auto load_stage = [&](int32_t j, int kbuf, int vbuf, bool do_k = true, bool do_v = true) {
         const int32_t key0 = j * BN;
         const int32_t nk = min(BN, k_end - key0);
         const char* kp = (const char*)a.k + 2 * (avf_elem_offset(k_tok0 + key0, a.k_row, h, a.k_head) + gseg * a.k_seg);
@@ -299,8 +303,8 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
             const int key = pos / T::ROWB;
             const int slot = (pos % T::ROWB) >> 4;
             const uint32_t kc = (uint32_t)min(key, nk - 1);
-            load_lds16(krs, kl + i * 1024, kc * k_rs + ((slot ^ k_swz<D>(key)) << 4));
-            load_lds16(vrs, vl + i * 1024, kc * v_rs + ((slot ^ v_swz<D>(key)) << 4));
+            if (do_k) load_lds16(krs, kl + i * 1024, kc * k_rs + ((slot ^ k_swz<D>(key)) << 4));
+            if (do_v) load_lds16(vrs, vl + i * 1024, kc * v_rs + ((slot ^ v_swz<D>(key)) << 4));
         }
     };
 
@@ -614,12 +618,23 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
         }
 #pragma unroll
         for (int kb = 0; kb < T::KB; ++kb) {
-            if (kb == T::KB - 2 && !LAST) {
+            // With two sub-blocks per stage (VLAG) the barrier is at sub-block
+            // 0, where V of stage j-1 is still read, so V stage j+1 (not j+2)
+            // is loaded there into the third V buffer; the last stage then
+            // needs its barrier too, to see its own V.
+            if (kb == T::KB - 2 && (!LAST || T::VLAG)) {
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
                 __syncthreads();
-                if (j + 2 < nkt) load_stage(j + 2, kbuf, vnext);
+                if (!LAST) {
+                    if constexpr (T::VLAG) {
+                        if (j + 2 < nkt) load_stage(j + 2, kbuf, 0, true, false);
+                        load_stage(j + 1, 0, (j + 1) % 3, false, true);
+                    } else {
+                        if (j + 2 < nkt) load_stage(j + 2, kbuf, vnext);
+                    }
 #pragma unroll
-                for (int u = 0; u < NKC; ++u) kcur[u] += kdelta;
+                    for (int u = 0; u < NKC; ++u) kcur[u] += kdelta;
+                }
             }
             // V reads move to stage j's buffer where they first read it: at
             // sub-block 1 (P.V(g-1) reads V of sub-block g-1), with F8 at
@@ -665,7 +680,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
 
     if (nkt > 0) {
         load_stage(0, 0, 0);
-        if (!ONE && nkt > 1) load_stage(1, 1, 1);
+        if (!ONE && nkt > 1) load_stage(1, 1, 1, true, !T::VLAG);
         // Wait for everything issued so far (Q fragments and the first two
         // stages), once per tile: the compiler does not see the stage loads,
         // so only a full vmcnt(0) tells it that the Q fragments have landed;
@@ -807,7 +822,7 @@ hipError_t launch_cfg(const AvfLaunchArgs& a, hipStream_t stream) {
     // grid: the exact tile count, or with a device plan the host's bound
     const dim3 grid((uint32_t)a.num_tiles), block(NW * 64);
     if (a.q8) {
-        if constexpr (D % 64 == 0 && !ONE) {
+        if constexpr (D % 64 == 0 && !ONE && BN >= 128) {  // the 8-bit path runs the general configuration
             if (a.causal)
                 hipLaunchKernelGGL((avf_fwd_kernel<D, QB, NW, BN, true, false, true, false>), grid, block, 0, stream, a);
             else
@@ -858,10 +873,19 @@ constexpr int block_m_of() { return Cfg<D>::QB * 32 * Cfg<D>::NW; }
 // 128 query rows, one 128-key K/V stage; two workgroups per CU.
 constexpr int kOneNW = 4, kOneStageKeys = 128;
 constexpr int kOneBlockM = 32 * kOneNW;
+// Short-stage configuration (segments of at most kShortStageKeys keys): 4
+// waves, 128 query rows, 64-key stages in rings of 2 K and 3 V buffers (80 KiB
+// at D = 128); two workgroups per CU.
+constexpr int kShortNW = 4, kShortBN = 64;
+// Measured against the general configuration on 56-head, D = 128 segments
+// of S keys: +26% at S = 256, +31% at 384, +4% at 512, even at 768-1024,
+// 2-3% slower from 2048 on (more barriers per key).
+constexpr int kShortStageKeys = 512;
 
 template <int D>
 hipError_t launch_d(const AvfLaunchArgs& a, hipStream_t stream) {
     if (a.one_stage) return launch_cfg<D, 1, kOneNW, kOneStageKeys, true>(a, stream);
+    if (a.short_stage) return launch_cfg<D, 1, kShortNW, kShortBN, false>(a, stream);
     return launch_cfg<D, Cfg<D>::QB, Cfg<D>::NW, Cfg<D>::BN, false>(a, stream);
 }
 
@@ -881,6 +905,8 @@ int32_t avf_block_m_one(int32_t head_dim) {
 }
 
 int32_t avf_one_stage_keys() { return kOneStageKeys; }
+
+int32_t avf_short_stage_keys() { return kShortStageKeys; }
 
 hipError_t avf_launch(const AvfLaunchArgs& a, int32_t head_dim, hipStream_t stream) {
     switch (head_dim) {

@@ -31,6 +31,8 @@ struct AvfLaunchArgs {
     int32_t causal;     // 1: query row r of a segment sees keys j <= r + Lk - Lq
     int32_t one_stage;  // 1: every segment has at most avf_one_stage_keys() keys (checked by
                         // the caller): the one-stage configuration, block_m avf_block_m_one
+    int32_t short_stage;  // 1 (one_stage 0): at most avf_short_stage_keys() keys: 64-key
+                          // stages, block_m avf_block_m_one
     // Device plan (sync-free entry): the planner's workspace (status, tile
     // count, tile prefix of all num_segs segments) and the caller's device
     // cu_seqlens; NULL for a host-planned launch, which uses the arrays below.
@@ -123,3 +125,4 @@ hipError_t avf_plan_launch(const int32_t* cu_q, const int32_t* cu_k, int32_t num
 int32_t avf_block_m(int32_t head_dim);
 int32_t avf_block_m_one(int32_t head_dim);
 int32_t avf_one_stage_keys();
+int32_t avf_short_stage_keys();
