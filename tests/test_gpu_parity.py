@@ -301,6 +301,34 @@ def test_stride_threshold_pair():
         torch.cuda.empty_cache()
 
 
+# The SM120 page's synthetic grid ("What rules things out": W windows x S
+# tokens at H = 8 and 56, varlen and batched-dense calls): its corners, with
+# the batched form equal to the varlen one bit for bit and sampled rows
+# against the oracle.
+W_BY_S = [(1, 1024, 8), (16, 1024, 56), (4, 4096, 56), (8, 24576, 8), (16, 4096, 8)]
+
+
+@pytest.mark.parametrize("W,S,H", W_BY_S)
+def test_pages_w_by_s_grid(W, S, H):
+    D = 128
+    announce(f"W x S grid W={W} S={S} H={H}")
+    torch.cuda.empty_cache()
+    w = custom(f"grid_{W}x{S}x{H}", H, D, [b * S for b in range(W + 1)], std=1.0)
+    t = make_inputs(w, DEV, seed=W + S + H)
+    o, l = run_gpu(t, w)
+    qb, kb, vb = (t[n].view(W, S, H, D) for n in ("q", "k", "v"))
+    ob, lb = avf.attn_fwd(qb, kb, vb)
+    torch.cuda.synchronize()
+    assert torch.equal(ob.reshape(W * S, H, D), o)
+    assert torch.equal(lb.permute(1, 0, 2).reshape(H, W * S), l[:, :W * S])
+    rows = sample_rows(w, 4, edge=1)
+    og, lg = gather(o, l, rows, w.total_q)
+    ro, rl = oracle_rows(t, w, rows, impl="blas")
+    compare(og, lg, ro, rl, w.name)
+    del t, o, l, ob, lb
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ softmax reference moves
 
 def _run_custom(q, k, v, cq, ck, label):
