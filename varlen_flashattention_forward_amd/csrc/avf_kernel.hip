@@ -4,6 +4,12 @@
 // streaming that segment's K/V in stages of BN keys through rings of LDS
 // buffers. K and V reach LDS by buffer loads that write LDS directly (no
 // registers, no LDS store instructions), one stage ahead of the compute.
+// Three configurations share this code (chosen on the host from max_seqlen_k):
+// the general one (8 waves, BM = 256, 128-key stages, one workgroup per CU),
+// and for short key segments, where the work is bound by memory latency
+// rather than MFMA, 4-wave workgroups (BM = 128) that share a CU in pairs:
+// one 128-key stage with one K and one V buffer (ONE, up to 128 keys) or
+// 64-key stages in 80 KiB rings (up to 512 keys).
 // The operation is the flash-attention varlen forward with its LSE
 // (the (out, lse) return of flash_attn_varlen_func on the "[FA4] cute varlen
 // backward: int32 overflow in _bwd_preprocess ..." page); the online softmax
