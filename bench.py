@@ -45,9 +45,14 @@ def log(*a):
 
 
 def kernel_hash() -> str:
+    """Hash of the forward kernel's code: its sources with // comments and
+    blank lines removed, so a comment edit keeps the committed counters."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        h.update((ROOT / p).read_bytes())
+        for line in (ROOT / p).read_text().splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
