@@ -56,6 +56,20 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def roofline_of(flops: int, nbytes: int, kernel_ms: float, peak_tflops: float) -> dict:
+    """Roofline figures of one launch: bound by MFMA when its arithmetic
+    intensity is at or above the ridge (peak FLOP/s over peak HBM bytes/s),
+    reported as TFLOP/s against `peak_tflops`; bound by HBM below it, reported
+    as algorithmic GB/s against the HBM peak."""
+    if flops / nbytes >= peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = flops / (kernel_ms / 1e3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak_tflops, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / peak_tflops, 4)}
+    gbs = nbytes / (kernel_ms / 1e3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def traffic_for(workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; else None."""
@@ -370,15 +384,9 @@ def main() -> int:
     if args.fp8:
         traffic = None  # the counters were taken on the bf16 kernel
     nbytes = w.algorithmic_bytes()
-    # the bound: MFMA above the ridge (peak FLOP/s over peak HBM bytes/s), HBM below it
-    if flops / nbytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
-                    "frac": round(achieved / peak, 4)}
-    else:
-        gbs = nbytes / launches / (kms / launches / 1e3) / 1e9
-        log(f"[bench] below the ridge ({flops / nbytes:.0f} flop/B): {gbs:.1f} GB/s of algorithmic bytes")
-        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    roofline = roofline_of(flops // launches, nbytes // launches, kms / launches, peak)
+    if roofline["bound"] == "hbm":
+        log(f"[bench] below the ridge ({flops / nbytes:.0f} flop/B): {roofline['achieved']} GB/s of algorithmic bytes")
     roofline.update({"traffic": traffic, "kernel_ms": round(kms / launches, 4),
                      "algorithmic_flops_per_launch": flops // launches,
                      "algorithmic_bytes_per_launch": nbytes // launches})

@@ -439,3 +439,36 @@ def test_fp8_rejects_host_errors_before_any_hip_call():
     assert call(ws=W + 16) == _binding.EALIGN
     assert call(nbytes=100) == _binding.EINVAL
     assert call(flags=8) == _binding.EINVAL
+
+
+def test_bench_roofline_bound_follows_the_ridge():
+    """bench.py reports MFMA-bound TFLOP/s at or above the ridge (2.5 PFLOP/s
+    over 8 TB/s = 312.5 flop/B) and HBM-bound GB/s of algorithmic bytes below it."""
+    import bench
+    d = WORKLOADS["dense_77k"]
+    r = bench.roofline_of(d.flops(), d.algorithmic_bytes(), 137.5, bench.PEAK_BF16_TFLOPS)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
+    assert abs(r["achieved"] - d.flops() / 0.1375 / 1e12) < 0.01
+    s = WORKLOADS["short_128"]
+    r = bench.roofline_of(s.flops(), s.algorithmic_bytes(), 0.116, bench.PEAK_BF16_TFLOPS)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert abs(r["achieved"] - s.algorithmic_bytes() / 0.116e-3 / 1e9) < 0.1
+    assert bench.roofline_of(312_500, 1000, 1.0, 2500.0)["bound"] == "mfma"
+    assert bench.roofline_of(312_499, 1000, 1.0, 2500.0)["bound"] == "hbm"
+
+
+def test_bench_kernel_hash_ignores_comments(tmp_path, monkeypatch):
+    """The key of the committed HBM counters follows the kernel's code, not
+    its comments."""
+    import shutil
+    import bench
+    for p in bench.KERNEL_SOURCES:
+        (tmp_path / p).parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(ROOT / p, tmp_path / p)
+    monkeypatch.setattr(bench, "ROOT", tmp_path)
+    h0 = bench.kernel_hash()
+    src = tmp_path / bench.KERNEL_SOURCES[0]
+    src.write_text("// a new comment line\n\n" + src.read_text().replace("\n", "  // trailing note\n", 1))
+    assert bench.kernel_hash() == h0
+    src.write_text(src.read_text() + "\nstatic int avf_extra_code;\n")
+    assert bench.kernel_hash() != h0
