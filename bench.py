@@ -327,14 +327,22 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
+    # per-step HIP events on the stream inside the timed region give the
+    # spread (median, min, max); the value is the wall-clock mean
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = elapsed / args.steps * 1e3
     value = flops / (ms / 1e3) / 1e12
-    log(f"[bench] {args.steps} steps: {ms:.3f} ms/step, {value:.1f} TFLOP/s")
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    spread = {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
+              "max": round(per_step[-1], 4)}
+    log(f"[bench] {args.steps} steps: {ms:.3f} ms/step, {value:.1f} TFLOP/s (per step {spread})")
 
     # kernel-only duration: HIP events on the launch stream around `steps`
     # back-to-back calls of the host cu_seqlens entry (no read-back inside the
@@ -406,6 +414,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms": spread,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
