@@ -137,15 +137,16 @@ struct Tile {
     static constexpr int NIK = KSBYTES / 1024;  // 1 KiB direct loads per K stage
     static constexpr int LDS_BYTES = KBUF * KSBYTES + VBUF * SBYTES;
     static constexpr int NI = SBYTES / 1024;    // 1 KiB direct loads per array and stage
-    static constexpr int NIW = NI / NW;         // ... per wave
-    static constexpr int LPS = 2 * NIW;         // direct loads per wave and stage (K and V)
     static_assert(D % 32 == 0 && BN % 32 == 0 && SBYTES % 1024 == 0, "tile shape");
     static_assert(KB >= 2 && KB % 2 == 0, "an even number of sub-blocks per stage (parity repeats every stage)");
     // Two sub-blocks per stage: the barrier sits at sub-block 0, where V of
     // the previous stage is still being read, so V stages load one stage
     // behind K (see `stage`).
     static constexpr bool VLAG = KB == 2;
-    static_assert(NI % NW == 0, "every wave issues the same number of loads per stage");
+    // Waves that issue the stage loads: with 8 waves only the first four
+    // (one per SIMD, the older wave of each SIMD's pair; see load_stage).
+    static constexpr int NL = NW == 8 ? NW / 2 : NW;
+    static_assert(NI % NL == 0 && (!F8 || NIK % NL == 0), "every loading wave issues the same number of loads");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS rings");
     static_assert(!F8 || (D % 64 == 0 && NIK % NW == 0), "8-bit K stages: depth-64 steps, whole loads per wave");
 };
@@ -277,13 +278,21 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
         const i32x4 vrs = rsrc_words(vp, (uint32_t)(nk - 1) * v_rs + 2 * D);
         const uint32_t kl = lds_addr + kbuf * T::KSBYTES;
         const uint32_t vl = lds_addr + T::KBUF * T::KSBYTES + vbuf * T::SBYTES;
+        // Only waves 0 .. NL-1 issue loads. The two waves of a SIMD do the
+        // same MFMA and softmax work per stage, and the older one wins
+        // every tie for the MFMA pipe, reaches the stage barrier first and
+        // waits there; giving it all of the pair's load issue (addresses,
+        // M0, the buffer loads) shortens the partner's path to the barrier:
+        // +2.8% on dense_77k, +2.3% on strided_9728, +3% on varlen_cross
+        // against all eight waves loading (the younger four loading: +0.5-1.3%).
+        if (wave >= T::NL) return;
         if constexpr (F8) {
             const uint32_t k8_rs = (uint32_t)(a.num_heads * D);
             const uint8_t* k8p = a.k8 + ((k_tok0 + key0) * a.num_heads + h) * D;
             const i32x4 k8rs = rsrc_words(k8p, (uint32_t)(nk - 1) * k8_rs + D);
 #pragma unroll
-            for (int m = 0; m < T::NIK / NW; ++m) {
-                const int i = wave + NW * m;
+            for (int m = 0; m < T::NIK / T::NL; ++m) {
+                const int i = wave + T::NL * m;
                 const int pos = i * 1024 + 16 * lane;
                 const int key = pos / T::KROWB;
                 const int slot = (pos % T::KROWB) >> 4;
@@ -291,8 +300,8 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
                 load_lds16(k8rs, kl + i * 1024, kc * k8_rs + ((slot ^ k8_swz<D>(key)) << 4));
             }
 #pragma unroll
-            for (int m = 0; m < T::NIW; ++m) {
-                const int i = wave + NW * m;
+            for (int m = 0; m < T::NI / T::NL; ++m) {
+                const int i = wave + T::NL * m;
                 const int pos = i * 1024 + 16 * lane;
                 const int key = pos / T::ROWB;
                 const int slot = (pos % T::ROWB) >> 4;
@@ -303,8 +312,8 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
         }
         const i32x4 krs = rsrc_words(kp, (uint32_t)(nk - 1) * k_rs + 2 * D);
 #pragma unroll
-        for (int m = 0; m < T::NIW; ++m) {
-            const int i = wave + NW * m;
+        for (int m = 0; m < T::NI / T::NL; ++m) {
+            const int i = wave + T::NL * m;
             const int pos = i * 1024 + 16 * lane;
             const int key = pos / T::ROWB;
             const int slot = (pos % T::ROWB) >> 4;
