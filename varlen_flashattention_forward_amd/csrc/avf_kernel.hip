@@ -658,6 +658,17 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
 #pragma unroll
                 for (int db = 0; db < T::DB; ++db) vcur[db] += vdelta;
             }
+            // D = 96 has the most softmax work per MFMA. Even with the stage
+            // loads on the older wave of each SIMD pair, the older wave still
+            // wins too many MFMA ties there, so the younger wave gets the
+            // higher priority for sub-block 0 of every stage: strided_9728
+            // +2%. At D = 128 the same costs 1%, so there it stays off.
+            if constexpr (NW == 8 && D == 96 && !F8) {
+                if (wave >= NW / 2 && kb == 0)
+                    __builtin_amdgcn_s_setprio(1);
+                else
+                    __builtin_amdgcn_s_setprio(0);
+            }
             if (MASKED) mask(kb, lim, sc[kb & 1]);
             float psum[QB];
             // sub-block g-1 has the other parity
