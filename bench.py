@@ -256,6 +256,9 @@ def main() -> int:
     ap.add_argument("--cpu-rows-bwd", type=int, default=8, help="dq rows per segment for the backward CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (scales HBM counters)")
+    ap.add_argument("--copy-rate", type=int, default=0, metavar="MIB",
+                    help="only time a plain device-to-device copy of MIB MiB (--warmup, then --steps copies) and "
+                         "print its read + write GB/s: the rate a plain stream reaches on this GPU")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library runs on a single MI355X and has no "
@@ -281,6 +284,24 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"[bench] copied {n} bytes 3 times")
+        return 0
+    if args.copy_rate:
+        n = args.copy_rate << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+        print(json.dumps({"metric": "device-to-device copy, read + write bytes per second", "value": 2 * n / ms / 1e6,
+                          "unit": "GB/s", "mib": args.copy_rate, "ms_per_copy": ms, "steps": args.steps,
+                          "warmup": args.warmup}), flush=True)
         return 0
     w = WORKLOADS[args.workload]
     avf.lib()
