@@ -108,6 +108,24 @@ def test_grid_plan_splits_long_segment_lists():
         assert launches == math.ceil(len(lens) / spl)
 
 
+def test_grid_plan_keeps_each_launch_below_2_to_32_work_items():
+    # eight-wave workgroups (512 threads): a launch holds at most 2^23 - 1
+    # tiles. Two segments of 2^27 rows at H = 8 and 256-row tiles make 2^23
+    # tiles, so they take two launches; a segment that alone needs more tiles
+    # than one launch holds is rejected.
+    bm = avf.block_m(128)
+    assert bm == 256
+    n = 1 << 27
+    launches, wgs = avf.grid_plan([0, n, 2 * n], 8, 128, n)
+    assert wgs == 2 * 8 * (n // bm) == 1 << 23
+    assert launches == 2
+    launches, wgs = avf.grid_plan([0, n - bm, 2 * n - bm], 8, 128, n)
+    assert wgs == (1 << 23) - 8 and launches == 1
+    with pytest.raises(avf.AttnVarlenError) as e:
+        avf.grid_plan([0, 2 * n], 16, 128, 2 * n)
+    assert e.value.code == _binding.EUNSUPPORTED
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_decode_is_a_bijection_onto_valid_tiles(seed):
     rng = random.Random(seed)

@@ -196,9 +196,10 @@ int64_t fill_plan(AvfLaunchArgs& a, const int32_t* cu_q, const int32_t* cu_k, in
     return t;
 }
 
-// Largest tile count one launch may have: grid size in work-items must stay
-// below 2^32 (HSA dispatch limit) with 256 threads per workgroup.
-constexpr int64_t kMaxTilesPerLaunch = (int64_t)1 << 23;
+// Largest tile count one launch may have: the grid size in work-items must
+// stay below 2^32 (HSA dispatch limit) with the largest workgroup any tile
+// kernel uses, 512 threads (the forward's eight waves).
+constexpr int64_t kMaxTilesPerLaunch = ((int64_t)1 << 32) / 512 - 1;
 
 // Forward configuration from the call's max_seqlen_k (which bounds every key
 // segment: checked against cu_seqlens on the host, or by the device planner):
@@ -460,6 +461,9 @@ int32_t attn_varlen_grid_plan(const int32_t* cu_q, int32_t B, int32_t H, int32_t
         while (b1 < B && b1 - b0 < AVF_SEGS_PER_LAUNCH) {
             const int64_t tb = tiles_of(cu_q, b1, b1 + 1, H, bm);
             if (t + tb > kMaxTilesPerLaunch && b1 > b0) break;
+            if (tb > kMaxTilesPerLaunch)
+                return fail(ATTN_VARLEN_EUNSUPPORTED, "segment %d needs %lld tiles (limit %lld per launch)",
+                            b1, (long long)tb, (long long)kMaxTilesPerLaunch);
             t += tb;
             ++b1;
         }
