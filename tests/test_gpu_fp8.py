@@ -119,20 +119,19 @@ def test_fp8_rejects_head_dim_96():
     assert e.value.code == _binding.EUNSUPPORTED
 
 
-def test_fp8_full_size_sampled_heads():
-    """dense_77k: sampled rows of three heads against the oracle, which
-    quantizes those heads alone (the scales are per head)."""
+def test_fp8_full_size_sampled():
+    """dense_77k: 4096 seeded rows compared in full (every head) against the
+    oracle, which quantizes q and k per head as the library does."""
     w = WORKLOADS["dense_77k"]
     announce("fp8 full size dense_77k")
     t = make_inputs(w, "cuda", seed=0)
     o, l, _ = run_fp8(t, w)
-    heads = [0, 27, 55]
-    rows = sample_rows(w, 48, edge=8)
-    qh, kh, vh = (t[n][:, heads].contiguous().cpu() for n in ("q", "k", "v"))
-    ro, rl = fp8_oracle.attn_varlen_fwd_fp8(qh, kh, vh, w.cu_q, w.cu_k, f32(w.softmax_scale), rows=rows)
+    rows = sample_rows(w, 4096, edge=16)
+    q, k, v = (t[n].contiguous().cpu() for n in ("q", "k", "v"))
+    ro, rl = fp8_oracle.attn_varlen_fwd_fp8(q, k, v, w.cu_q, w.cu_k, f32(w.softmax_scale), rows=rows)
     idx = torch.tensor(rows, device="cuda")
-    go = o.index_select(0, idx)[:, heads].float().cpu().numpy()
-    gl = l[heads][:, rows].t().cpu().numpy()
+    go = o.index_select(0, idx).float().cpu().numpy()
+    gl = l[:, :w.total_q][:, rows].t().cpu().numpy()
     st = compare(go, gl, ro, rl, "fp8 dense_77k")
     print(f"[fp8 dense_77k] {st}", flush=True)
 

@@ -263,6 +263,9 @@ def test_bad_device_cu_is_rejected_without_writing():
 # ------------------------------------------------------------------ full-size workloads (sampled rows)
 
 FULL = ["varlen_cross", "dense_77k", "strided_9728", "dense_117k"]
+# seeded query rows per segment compared in full (every head, every column) at
+# the full sizes: a segment with fewer rows is compared whole
+FULL_SAMPLE = 4096
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -275,7 +278,7 @@ def test_full_size_sampled(name):
     if w.layout == "stride9728":
         hd = w.num_heads * w.head_dim
         assert bool((t["out_base"][:, hd:] == CANARY).all()), "write outside the O slice"
-    rows = sample_rows(w, 64, edge=16)
+    rows = sample_rows(w, FULL_SAMPLE, edge=16)
     og, lg = gather(o, l, rows, w.total_q)
     ro, rl = oracle_rows(t, w, rows, impl="blas")
     stats = compare(og, lg, ro, rl, name)
