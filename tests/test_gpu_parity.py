@@ -262,7 +262,7 @@ def test_bad_device_cu_is_rejected_without_writing():
 
 # ------------------------------------------------------------------ full-size workloads (sampled rows)
 
-FULL = ["varlen_cross", "dense_77k", "strided_9728", "dense_117k"]
+FULL = ["varlen_cross", "dense_77k", "strided_9728", "dense_117k", "shard_heads_117k", "shard_rows_117k"]
 # seeded query rows per segment compared in full (every head, every column) at
 # the full sizes: a segment with fewer rows is compared whole
 FULL_SAMPLE = 4096

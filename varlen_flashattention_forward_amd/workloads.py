@@ -126,6 +126,10 @@ WORKLOADS = {
     "short_128": Workload("short_128", 56, 128, _cu_uniform(64, 128), _cu_uniform(64, 128), 0.1, True),
     "short_256": Workload("short_256", 56, 128, _cu_uniform(64, 256), _cu_uniform(64, 256), 0.1, True),
     "short_512": Workload("short_512", 56, 128, _cu_uniform(64, 512), _cu_uniform(64, 512), 0.1, True),
+    # one GPU's share of dense_117k split eight ways: by heads (7 of 56), or by
+    # query rows (context parallel: 14625 rows against all 117000 keys)
+    "shard_heads_117k": Workload("shard_heads_117k", 7, 128, (0, 117000), (0, 117000), 1.0, True),
+    "shard_rows_117k": Workload("shard_rows_117k", 56, 128, (0, 14625), (0, 117000), 1.0, False),
     # backward: contiguous q, k, v; dout an [N, H, D] view of an [N, 9728] buffer (make_dout)
     "bwd_9728": Workload("bwd_9728", 16, 96, (0, 225304, 410923), (0, 225304, 410923), 0.1, True,
                          outer_stride=9728),
