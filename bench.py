@@ -20,6 +20,7 @@ of the forward's size; the kernels form S and dP twice, so they execute 14).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -256,6 +257,8 @@ def main() -> int:
     ap.add_argument("--cpu-rows-bwd", type=int, default=8, help="dq rows per segment for the backward CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (scales HBM counters)")
+    ap.add_argument("--head-major", action="store_true",
+                    help="the workload's q, k, v and out as head-major views (row stride D, head stride tokens*D)")
     ap.add_argument("--copy-rate", type=int, default=0, metavar="MIB",
                     help="only time a plain device-to-device copy of MIB MiB (--warmup, then --steps copies) and "
                          "print its read + write GB/s: the rate a plain stream reaches on this GPU")
@@ -304,6 +307,11 @@ def main() -> int:
                           "warmup": args.warmup}), flush=True)
         return 0
     w = WORKLOADS[args.workload]
+    if args.head_major:
+        if w.layout != "contiguous":
+            print(f"--head-major needs a contiguous workload ({w.name} is {w.layout})", file=sys.stderr)
+            return 2
+        w = dataclasses.replace(w, layout="head_major")
     avf.lib()
     log(f"[bench] workload {w.name}: H={w.num_heads} D={w.head_dim} segments={w.num_segments} "
         f"total_q={w.total_q} total_k={w.total_k}")
@@ -408,7 +416,7 @@ def main() -> int:
                                           w.max_seqlen_k)
     achieved = flops / launches / (kms / launches / 1e3) / 1e12
     log(f"[bench] kernel: {kms:.3f} ms/call over {launches} launch(es), {wgs} workgroups, {achieved:.1f} TFLOP/s")
-    traffic = traffic_for(w.name)
+    traffic = traffic_for(w.name) if w.layout == "contiguous" else None  # counters: token-major runs
     peak = PEAK_FP8_QK_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
     if args.fp8:
         traffic = None  # the counters were taken on the bf16 kernel

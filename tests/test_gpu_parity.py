@@ -146,6 +146,39 @@ def test_strided_equals_contiguous_bitwise_and_canaries():
     compare(og, lg, ro, rl, "strided_small")
 
 
+# key lengths that select each configuration: one 128-key stage, 64-key stages, general
+HEAD_MAJOR_CASES = [(64, [0, 77, 77, 300, 301], [0, 128, 129, 200, 256], False),
+                    (128, [0, 500, 520, 900], [0, 400, 912, 1024], True),
+                    (96, [0, 640, 641, 1400], [0, 700, 1300, 1301], False),
+                    (128, [0, 1000, 1030], [0, 1500, 1700], True)]
+
+
+@pytest.mark.parametrize("D,cu_q,cu_k,causal", HEAD_MAJOR_CASES)
+def test_head_major_views_equal_token_major_bitwise(D, cu_q, cu_k, causal):
+    """The same values stored head by head ([H, tokens, D] buffers seen as
+    [tokens, H, D] views: row stride D, head stride tokens * D) give the
+    token-major results bit for bit, and match the oracle."""
+    H = 3
+    wt = custom(f"token_d{D}", H, D, cu_q, cu_k, std=1.0, causal=causal)
+    wh = custom(f"head_d{D}", H, D, cu_q, cu_k, std=1.0, layout="head_major", causal=causal)
+    announce(f"head-major vs token-major D={D} causal={causal} max_k={wt.max_seqlen_k}")
+    tt = make_inputs(wt, DEV, seed=9)
+    th = make_inputs(wh, DEV, seed=9)
+    assert th["q"].stride() == (D, wh.total_q * D, 1) and torch.equal(th["q"], tt["q"])
+    kw = dict(softmax_scale=wt.softmax_scale, causal=causal)
+    ot, lt = avf.attn_varlen_fwd(tt["q"], tt["k"], tt["v"], tt["cu_q"], tt["cu_k"], wt.max_seqlen_q,
+                                 wt.max_seqlen_k, out=tt["out"], lse=tt["lse"], **kw)
+    oh, lh = avf.attn_varlen_fwd(th["q"], th["k"], th["v"], th["cu_q"], th["cu_k"], wh.max_seqlen_q,
+                                 wh.max_seqlen_k, out=th["out"], lse=th["lse"], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(ot, oh) and torch.equal(lt, lh)
+    rows = list(range(wt.total_q))
+    og, lg = gather(ot, lt, rows, wt.total_q)
+    q, k, v = (tt[n].contiguous().cpu() for n in ("q", "k", "v"))
+    ro, rl = oracle.attn_varlen_fwd(q, k, v, wt.cu_q, wt.cu_k, f32(wt.softmax_scale), rows=rows, causal=causal)
+    compare(og, lg, ro, rl, wh.name)
+
+
 def test_deterministic_and_hostcu_bitwise():
     w = SMALL["ragged_d128"]
     announce("determinism + host cu_seqlens entry")

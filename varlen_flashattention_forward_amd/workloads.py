@@ -49,7 +49,7 @@ class Workload:
     cu_k: tuple
     std: float
     self_attention: bool        # cu_q == cu_k, q/k/v drawn together
-    layout: str = "contiguous"  # or "stride9728"
+    layout: str = "contiguous"  # or "stride9728", or "head_major"
     outer_stride: int = 0       # elements per token row of the shared buffer
     causal: bool = False        # row r of a segment sees keys j <= r + Lk - Lq
     notes: str = field(default="", compare=False)
@@ -192,8 +192,17 @@ def make_inputs(w: Workload, device="cuda", seed: int = 0, lse_head_pad: int = 0
                 q.mul_(w.std)
                 k.mul_(w.std)
                 v.mul_(w.std)
-        out_base = torch.full((w.total_q, H, D), CANARY, dtype=bf, device=device)
-        out = out_base
+        if w.layout == "head_major":
+            # the same values stored head by head: [H, tokens, D] buffers seen
+            # as [tokens, H, D] views (row stride D, head stride tokens * D)
+            q, k, v = (x.permute(1, 0, 2).contiguous().permute(1, 0, 2) for x in (q, k, v))
+            out_base = torch.full((H, w.total_q, D), CANARY, dtype=bf, device=device)
+            out = out_base.permute(1, 0, 2)
+        elif w.layout == "contiguous":
+            out_base = torch.full((w.total_q, H, D), CANARY, dtype=bf, device=device)
+            out = out_base
+        else:
+            raise ValueError(f"unknown layout {w.layout!r}")
     lse = torch.full((H, w.total_q + lse_head_pad), CANARY, dtype=torch.float32, device=device)
     cu_q = torch.tensor(w.cu_q, dtype=torch.int32, device=device)
     cu_k = torch.tensor(w.cu_k, dtype=torch.int32, device=device)
