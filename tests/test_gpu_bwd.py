@@ -180,6 +180,32 @@ def test_bwd_output_strides(D):
         assert bool((b[mask] == -7.0).all())
 
 
+@pytest.mark.parametrize("D,causal", [(64, False), (96, True), (128, False), (128, True)])
+def test_bwd_head_major_views_bitwise(D, causal):
+    """q, k, v, out, dout and dq/dk/dv all as head-major views ([H, tokens, D]
+    buffers seen as [tokens, H, D]: row stride D, head stride tokens * D): the
+    gradients equal the token-major ones bit for bit."""
+    announce(f"bwd head-major views D={D} causal={causal}")
+    cu_q, cu_k = [0, 150, 151, 420], [0, 200, 200, 333]
+    wt = custom(f"bt{D}", 3, D, cu_q, cu_k, std=1.0)
+    wh = custom(f"bh{D}", 3, D, cu_q, cu_k, std=1.0, layout="head_major")
+    tt = make_inputs(wt, "cuda", seed=21)
+    th = make_inputs(wh, "cuda", seed=21)
+    dout, _ = make_dout(wt, "cuda", seed=22)
+
+    def head_major(x):
+        return x.permute(1, 0, 2).contiguous().permute(1, 0, 2)
+
+    a = backward(tt, wt, dout, causal)
+    H = wt.num_heads
+    outs = [torch.empty((H, n, D), dtype=torch.bfloat16, device="cuda").permute(1, 0, 2)
+            for n in (wt.total_q, wt.total_k, wt.total_k)]
+    b = backward(th, wh, head_major(dout), causal, dq=outs[0], dk=outs[1], dv=outs[2])
+    assert outs[0].stride() == (D, wt.total_q * D, 1)
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x, y)
+
+
 # ------------------------------------------------------------------ the page's full-size case
 
 def test_bwd_full_size_strided_dout():
