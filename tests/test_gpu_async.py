@@ -200,3 +200,21 @@ def test_sync_free_strided_views():
     torch.cuda.synchronize()
     assert avf.async_status(ws) == 0
     assert torch.equal(a_o, b_o) and torch.equal(a_l[:, :w.total_q], b_l[:, :w.total_q])
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_sync_free_head_major_views(causal):
+    """Head-major views (row stride D, head stride tokens * D) of q, k, v and
+    out through the sync-free entry: equal to the host-planned token-major
+    results bit for bit."""
+    announce(f"sync-free head-major causal={causal}")
+    cu_q, cu_k = [0, 300, 301, 1000], [0, 128, 700, 1500]
+    wt = custom("async_tm", 3, 128, cu_q, cu_k, std=1.0)
+    wh = custom("async_hm", 3, 128, cu_q, cu_k, std=1.0, layout="head_major")
+    tt, th = make_inputs(wt, "cuda", seed=8), make_inputs(wh, "cuda", seed=8)
+    a_o, a_l = host_planned(tt, wt, causal)
+    b_o, b_l, ws = sync_free(th, wh, causal)
+    torch.cuda.synchronize()
+    assert avf.async_status(ws) == 0
+    assert b_o.stride() == (128, wh.total_q * 128, 1)
+    assert torch.equal(a_o, b_o) and torch.equal(a_l[:, :wt.total_q], b_l[:, :wt.total_q])

@@ -137,8 +137,9 @@ def test_fp8_full_size_sampled():
 
 
 def test_fp8_strided_views_equal_contiguous():
-    """q, k, v as views of wider buffers (row stride 3*H*D + 64): the same
-    codes and outputs as their contiguous copies."""
+    """q, k, v as views of wider buffers (row stride 3*H*D + 64), and as
+    head-major views (row stride D, head stride tokens * D, out too): the same
+    outputs as their contiguous copies."""
     announce("fp8 strided views")
     w = custom("fp8_strided", 4, 128, [0, 333, 900], [0, 500, 1200], std=1.0)
     H, D = 4, 128
@@ -154,6 +155,13 @@ def test_fp8_strided_views_equal_contiguous():
         t[n] = t[n].contiguous()
     b, bl, _ = run_fp8(t, w)
     assert torch.equal(a, b) and torch.equal(al[:, :w.total_q], bl[:, :w.total_q])
+    b, bl = b.clone(), bl.clone()
+    for n in ("q", "k", "v"):
+        t[n] = t[n].permute(1, 0, 2).contiguous().permute(1, 0, 2)
+    t["out"] = torch.empty((H, w.total_q, D), dtype=torch.bfloat16, device="cuda").permute(1, 0, 2)
+    c, cl, _ = run_fp8(t, w)
+    assert c.stride() == (D, w.total_q * D, 1)
+    assert torch.equal(c, b) and torch.equal(cl[:, :w.total_q], bl[:, :w.total_q])
 
 
 def test_fp8_many_segments_span_launches():
