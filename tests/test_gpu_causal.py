@@ -230,6 +230,24 @@ def test_batched_strided_layouts(causal):
             l.permute(1, 0, 2).reshape(H, W * Sq).t().cpu().numpy(), oo, ol, f"batched strided causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_batched_sdpa_layout_views(causal):
+    """q, k, v and out stored [W, H, S, D] (the layout of torch's
+    scaled_dot_product_attention) and passed as [W, S, H, D] views: the same
+    results, bit for bit, as contiguous [W, S, H, D] copies."""
+    announce(f"batched [W, H, S, D] storage (causal={causal})")
+    W, Sq, Sk, H, D = 3, 300, 520, 4, 128
+    q = rand_bf16((W, H, Sq, D), seed=41).transpose(1, 2)
+    k = rand_bf16((W, H, Sk, D), seed=42).transpose(1, 2)
+    v = rand_bf16((W, H, Sk, D), seed=43).transpose(1, 2)
+    out = torch.empty((W, H, Sq, D), dtype=torch.bfloat16, device=DEV).transpose(1, 2)
+    o, l = avf.attn_fwd(q, k, v, causal=causal, out=out)
+    oc, lc = avf.attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), causal=causal)
+    torch.cuda.synchronize()
+    assert o.stride() == (H * Sq * D, D, Sq * D, 1)
+    assert torch.equal(o, oc) and torch.equal(l, lc)
+
+
 def test_batched_many_batches_span_launches():
     """More batches than segments per launch: later launches must address
     their batches from the right base."""
