@@ -46,7 +46,8 @@ extern "C" {
 #define ATTN_VARLEN_OK 0
 #define ATTN_VARLEN_ENULL (-1)        /* a required pointer is NULL */
 #define ATTN_VARLEN_EINVAL (-2)       /* bad count, stride, scale or overlapping output */
-#define ATTN_VARLEN_EUNSUPPORTED (-3) /* head_dim not in {64, 96, 128}, stride over limit */
+#define ATTN_VARLEN_EUNSUPPORTED (-3) /* head_dim not in {64, 96, 128}, stride over limit, or one
+                                         segment needing more tiles than a launch holds (2^23 - 1) */
 #define ATTN_VARLEN_EALIGN (-4)       /* pointer not 16-byte aligned / stride not a multiple of 8 */
 #define ATTN_VARLEN_ECU (-5)          /* cu_seqlens: cu[0] != 0, decreasing, or past the token extents */
 #define ATTN_VARLEN_EMAXSEQ (-6)      /* a segment is longer than max_seqlen_q / max_seqlen_k */
@@ -166,8 +167,11 @@ int64_t attn_varlen_count_tiles(const int32_t* cu_seqlens_q_host, int32_t num_se
  * Number of kernel launches and workgroups attn_varlen_fwd would use for
  * these host cu_seqlens_q and this max_seqlen_k (which picks the tile
  * height, attn_varlen_block_m_for). Segments are split into launches of at
- * most attn_varlen_segments_per_launch() segments; each launch's grid is
- * exactly its tile count. Writes the totals to *launches and *workgroups.
+ * most attn_varlen_segments_per_launch() segments and at most 2^23 - 1 tiles
+ * (a launch of 512-thread workgroups stays below 2^32 work-items); each
+ * launch's grid is exactly its tile count. Writes the totals to *launches
+ * and *workgroups. Returns ATTN_VARLEN_EUNSUPPORTED, as the forward does,
+ * when one segment alone needs more tiles than a launch holds.
  */
 int32_t attn_varlen_grid_plan(const int32_t* cu_seqlens_q_host, int32_t num_segments,
                               int32_t num_heads, int32_t head_dim, int32_t max_seqlen_k,
