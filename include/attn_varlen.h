@@ -119,6 +119,12 @@ int32_t attn_varlen_fwd_hostcu(const void* q, const void* k, const void* v,
  * Argument check of attn_varlen_fwd_hostcu without any HIP call: returns the
  * code that call would return before launching. Pointers are only checked
  * for NULL and alignment, never dereferenced (cu arrays are host arrays).
+ * The check refuses what the SM120 page's faults come from ("compute-sanitizer
+ * memcheck findings", "Interpretation"): cu_seqlens that do not start at 0,
+ * decrease, exceed max_seqlen_q/k or index past q_tokens/k_tokens, and
+ * strides that would make out overlap itself or exceed the per-tile 32-bit
+ * lane offsets (row stride <= ATTN_VARLEN_MAX_ROW_STRIDE); any other error
+ * of the call is a HIP runtime failure (ATTN_VARLEN_EHIP).
  */
 int32_t attn_varlen_validate(const void* q, const void* k, const void* v,
                              const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_k_host,
@@ -164,6 +170,21 @@ int64_t attn_varlen_count_tiles(const int32_t* cu_seqlens_q_host, int32_t num_se
                                 int32_t num_heads, int32_t block_m);
 
 /*
+ * Exact workgroup total of one attn_varlen_fwd / attn_varlen_fwd_hostcu call
+ * with these host cu_seqlens_q, num_heads, head_dim and max_seqlen_k:
+ * H * sum_b ceil(Lq_b / BM) with BM = attn_varlen_block_m_for(head_dim,
+ * max_seqlen_k), summed over the call's launches. This is the per-segment
+ * ceil tile accounting of the SM120 page ("Interpretation"), whose launched
+ * grid exceeded the valid tile count; here the grid equals this count (15680
+ * for that page's cu_seqlens_q at BM = 128 and H = 56). Returns a negative
+ * ATTN_VARLEN_E* code on bad arguments (NULL, H <= 0, cu not starting at 0
+ * or decreasing, unsupported head_dim, max_seqlen_k < 0, or a segment larger
+ * than one launch holds).
+ */
+int64_t attn_varlen_num_tiles(const int32_t* cu_seqlens_q_host, int32_t num_segments,
+                              int32_t num_heads, int32_t head_dim, int32_t max_seqlen_k);
+
+/*
  * Number of kernel launches and workgroups attn_varlen_fwd would use for
  * these host cu_seqlens_q and this max_seqlen_k (which picks the tile
  * height, attn_varlen_block_m_for). Segments are split into launches of at
@@ -196,7 +217,12 @@ int32_t attn_varlen_decode_tile(const int32_t* cu_seqlens_q_host, int32_t num_se
 int64_t attn_varlen_element_offset(int64_t row, int64_t row_stride, int64_t head,
                                    int64_t head_stride);
 
-/* Message for the last non-zero return on the calling thread ("" if none). */
+/*
+ * Message for the last non-zero return on the calling thread ("" if none).
+ * Every entry point reports failure by a code instead of the assertion abort
+ * of the ffpa-attn PR #387 page ("Problem": a TMA descriptor assertion ends
+ * the process); this gives the reason in words.
+ */
 const char* attn_varlen_last_error(void);
 
 /*
@@ -243,8 +269,8 @@ int32_t attn_varlen_validate_ex(const void* q, const void* k, const void* v,
  *
  * The batched call form flash_attn_func on [W, S, H, D] views, which the
  * "[FA4][SM120] flash_attn_varlen_func ... illegal memory access at >=4 varlen
- * segments" page runs next to the varlen form ("What rules things out":
- * "varlen and batched-dense (flash_attn_func on [W, S, H, D] views)"). It is
+ * segments" page exercises next to the varlen form in its synthetic sweep
+ * ("What rules things out"). It is
  * the varlen operation with W segments of seqlen_q query rows and seqlen_k
  * key rows each; batch b of q/k/v/out is that segment.
  *
@@ -281,10 +307,10 @@ int32_t attn_fwd_batched_validate(const void* q, const void* k, const void* v, i
  *
  * attn_varlen_fwd with device cu_seqlens and NO host synchronisation: the
  * call enqueues two kernels on `stream` and returns. Why: the FA4 SM120 page
- * stresses the kernel's speed on small inputs ("~7x faster than our fallback
- * for small inputs") where a per-call device-to-host read-back of cu_seqlens
- * costs as much as the attention itself, and a call without host waits can be
- * captured in a HIP graph.
+ * (its opening motivation) values the kernel most for small inputs, where a
+ * per-call device-to-host read-back of cu_seqlens costs as much as the
+ * attention itself, and a call without host waits can be captured in a HIP
+ * graph.
  *   1. A one-workgroup planner kernel checks cu_seqlens on the device (start
  *      at 0, non-decreasing, segments within max_seqlen_q/k, ends within
  *      q_tokens/k_tokens) and writes the tile prefix into `workspace`.

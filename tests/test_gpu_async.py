@@ -1,18 +1,44 @@
 """GPU tests of the sync-free forward (device planner + bounded, looping
-grid): bitwise agreement with the host-planned path, one launch for any
-number of segments, invalid cu_seqlens values reported through the
-workspace status with the outputs untouched, and capture in a HIP graph.
-Marked `gpu`; every case prints its name before it touches the GPU.
+grid): its outputs against the CPU oracle at the parity bar (small cases in
+full, larger ones on seeded rows, the SM120 page's varlen_cross call at full
+size on 4096 rows per segment), bitwise agreement with the host-planned path,
+one launch for any number of segments, invalid cu_seqlens values reported
+through the workspace status with the outputs untouched, and capture in a HIP
+graph. Marked `gpu`; every case prints its name before it touches the GPU.
 """
 import numpy as np
 import pytest
 import torch
 
+import oracle
+from oracle import blas_oracle
 import varlen_flashattention_forward_amd as avf
 from varlen_flashattention_forward_amd import _binding
-from varlen_flashattention_forward_amd.workloads import CANARY, custom, make_inputs
+from varlen_flashattention_forward_amd.workloads import CANARY, WORKLOADS, custom, make_inputs, sample_rows
+
+from parity import compare
 
 pytestmark = pytest.mark.gpu
+
+
+def f32(x):
+    """The fp32 value the library receives, widened for the oracle."""
+    return float(np.float32(x))
+
+
+def check_oracle(o, l, t, w, causal=False, rows=None, impl="c", label=""):
+    """The sync-free outputs o [total_q, H, D], l [H, >= total_q] on the given
+    global query rows (all if None) against the oracle at the parity bar."""
+    rows = list(range(w.total_q)) if rows is None else rows
+    idx = torch.tensor(rows, dtype=torch.long, device=o.device)
+    og = o.index_select(0, idx).float().cpu().numpy()
+    lg = l[:, :w.total_q].index_select(1, idx).t().cpu().numpy()
+    q, k, v = (t[n].contiguous().cpu() for n in ("q", "k", "v"))
+    fn = oracle.attn_varlen_fwd if impl == "c" else blas_oracle.attn_varlen_fwd
+    ro, rl = fn(q, k, v, w.cu_q, w.cu_k, f32(w.softmax_scale), rows=rows, causal=causal)
+    stats = compare(og, lg, ro, rl, label or w.name)
+    print(f"[gpu-case] {label or w.name} oracle {stats}", flush=True)
+    return stats
 
 
 def announce(label):
@@ -71,6 +97,7 @@ def test_sync_free_equals_host_planned(name, causal):
     b_o, b_l, ws = sync_free(t, w, causal)
     torch.cuda.synchronize()
     assert avf.async_status(ws) == 0
+    check_oracle(b_o, b_l, t, w, causal)
     assert torch.equal(a_o, b_o)
     assert torch.equal(a_l[:, :w.total_q], b_l[:, :w.total_q])
 
@@ -87,6 +114,7 @@ def test_sync_free_many_segments_one_launch():
     b_o, b_l, ws = sync_free(t, w)
     torch.cuda.synchronize()
     assert avf.async_status(ws) == 0
+    check_oracle(b_o, b_l, t, w)
     assert torch.equal(a_o, b_o) and torch.equal(a_l[:, :w.total_q], b_l[:, :w.total_q])
 
 
@@ -111,6 +139,7 @@ def test_sync_free_segment_search_boundaries(B):
     b_o, b_l, ws = sync_free(t, w)
     torch.cuda.synchronize()
     assert avf.async_status(ws) == 0
+    check_oracle(b_o, b_l, t, w)
     assert torch.equal(a_o, b_o) and torch.equal(a_l[:, :w.total_q], b_l[:, :w.total_q])
 
 
@@ -126,6 +155,7 @@ def test_sync_free_grid_smaller_than_tile_count_loops():
     b_o, b_l, ws = sync_free(t, w)
     torch.cuda.synchronize()
     assert avf.async_status(ws) == 0
+    check_oracle(b_o, b_l, t, w, rows=sample_rows(w, 2048, edge=16), impl="blas")
     assert torch.equal(a_o, b_o) and torch.equal(a_l[:, :w.total_q], b_l[:, :w.total_q])
 
 
@@ -187,6 +217,7 @@ def test_sync_free_in_a_hip_graph():
         torch.cuda.synchronize()
         assert torch.equal(o, ref_o), rep
         assert torch.equal(l[:, :w.total_q], ref_l[:, :w.total_q]), rep
+        check_oracle(o, l, t, w, label=f"graph replay {rep}")
 
 
 def test_sync_free_strided_views():
@@ -199,6 +230,7 @@ def test_sync_free_strided_views():
     b_o, b_l, ws = sync_free(t, w)
     torch.cuda.synchronize()
     assert avf.async_status(ws) == 0
+    check_oracle(b_o, b_l, t, w)
     assert torch.equal(a_o, b_o) and torch.equal(a_l[:, :w.total_q], b_l[:, :w.total_q])
 
 
@@ -217,4 +249,25 @@ def test_sync_free_head_major_views(causal):
     torch.cuda.synchronize()
     assert avf.async_status(ws) == 0
     assert b_o.stride() == (128, wh.total_q * 128, 1)
+    check_oracle(b_o, b_l, th, wh, causal)
     assert torch.equal(a_o, b_o) and torch.equal(a_l[:, :wt.total_q], b_l[:, :wt.total_q])
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_sync_free_full_size_varlen_cross(causal):
+    """The SM120 page's captured call ("Bug 2 details": eight query windows
+    summing to 35280 rows against eight 17580-row key segments, H = 56,
+    D = 128) through the sync-free entry, the form that page's scheduler
+    fault concerns: 4096 seeded rows per segment (a shorter segment whole,
+    first and last 16 rows always) against the oracle, every head and column."""
+    w = WORKLOADS["varlen_cross"]
+    announce(f"sync-free full-size varlen_cross causal={causal}")
+    torch.cuda.empty_cache()
+    t = make_inputs(w, "cuda", seed=0)
+    o, l, ws = sync_free(t, w, causal)
+    torch.cuda.synchronize()
+    assert avf.async_status(ws) == 0
+    check_oracle(o, l, t, w, causal, rows=sample_rows(w, 4096, edge=16), impl="blas",
+                 label=f"sync-free varlen_cross causal={causal}")
+    del t, o, l
+    torch.cuda.empty_cache()

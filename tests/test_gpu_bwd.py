@@ -248,6 +248,44 @@ def test_bwd_full_size_strided_dout():
         assert bool(((sdv - sg).abs() <= tol_v).all()), s
 
 
+@pytest.mark.parametrize("split", [220752, 220753])
+def test_bwd_stride_threshold_pair_full_gradients(split):
+    """The _bwd_preprocess page's threshold ("Verified sample": coord * 9728
+    passes 2^31 from row 220753 on) as a pair of calls that differ only in
+    cu_seqlens: [0, split, split + 1536] with q, k, v, out, dout and the
+    outputs dq, dk, dv all [N, 16, 96] views of [N, 9728] buffers. The second
+    segment's rows start at element offset split * 9728, past 2^31 only for
+    split = 220753. Segments are independent, so that segment's dq, dk and dv
+    are compared in full against the oracle run on it alone; the long first
+    segment's gradients must be finite, and the columns of the output buffer
+    outside the three views must keep their canary."""
+    n2, H, D, R = 1536, 16, 96, 9728
+    N = split + n2
+    announce(f"bwd stride threshold split={split}")
+    torch.cuda.empty_cache()
+    w = custom(f"bthresh{split}", H, D, [0, split, N], std=0.1, layout="stride9728", outer_stride=R)
+    t = make_inputs(w, "cuda", seed=61)
+    dout, _ = make_dout(w, "cuda", seed=62, outer_stride=R)
+    assert dout.stride(0) == R and t["q"].stride(0) == R
+    assert (split * R >= 2 ** 31) == (split == 220753)
+    gbuf = torch.full((N, R), -7.0, dtype=torch.bfloat16, device="cuda")
+    hd = H * D
+    dq, dk, dv = (gbuf[:, i * hd:(i + 1) * hd].view(N, H, D) for i in range(3))
+    got = backward(t, w, dout, False, dq=dq, dk=dk, dv=dv)
+    assert got[0].data_ptr() == dq.data_ptr() and got[2].data_ptr() == dv.data_ptr()
+    assert bool((gbuf[:, 3 * hd:] == -7.0).all()), "write outside the gradient views"
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(g[:split]).all()), name
+    sl = slice(split, N)
+    q, k, v = (t[n][sl].contiguous().cpu() for n in ("q", "k", "v"))
+    rq, rk, rv = oracle.attn_varlen_bwd(q, k, v, dout[sl].contiguous().cpu(), [0, n2], [0, n2], f32(w.softmax_scale))
+    stats = {name: compare_grad(g[sl].float().cpu().numpy(), r, f"split={split} {name}")
+             for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv))}
+    print(f"[bwd threshold split={split}] second segment {stats}", flush=True)
+    del t, dout, gbuf, got
+    torch.cuda.empty_cache()
+
+
 def test_bwd_many_segments_span_launches():
     """200 short segments (some empty): the dK/dV and dQ plans split them over
     launches of 128 segments; gradients match the oracle everywhere."""

@@ -1,7 +1,8 @@
 """Seeded random sweeps of the other entry points through the C ABI:
 - the backward, with full gradients against the oracle's fp64 gradients;
 - the 8-bit score product, with sampled rows against the quantized oracle;
-- the sync-free forward, bitwise against the host-planned forward.
+- the sync-free forward, on sampled rows against the oracle and bitwise
+  against the host-planned forward.
 Cases draw random segment tables with empty segments, head counts, head_dims,
 the causal mask, and for the forward entries a loose or exact max_seqlen_k
 (so every configuration is hit). Marked `gpu`; every case prints its
@@ -120,4 +121,11 @@ def test_random_sync_free_bitwise(seed):
                                          lse=b_l, causal=causal)
     torch.cuda.synchronize()
     assert avf.async_status(ws) == 0
+    rows = sample_rows(w, 64, seed=seed, edge=8)
+    idx = torch.tensor(rows, dtype=torch.long, device=DEV)
+    og = b_o.index_select(0, idx).float().cpu().numpy()
+    lg = b_l[:, :w.total_q].index_select(1, idx).t().cpu().numpy()
+    q, k, v = (t[n].cpu() for n in ("q", "k", "v"))
+    ro, rl = oracle.attn_varlen_fwd(q, k, v, w.cu_q, w.cu_k, f32(w.softmax_scale), rows=rows, causal=causal)
+    compare(og, lg, ro, rl, w.name)
     assert torch.equal(a_o, b_o) and torch.equal(a_l, b_l)

@@ -130,6 +130,7 @@ def test_short_configs_sync_free_bitwise(kind, causal):
         _, _, ws = avf.attn_varlen_fwd_async(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], w.max_seqlen_q, max_k,
                                              softmax_scale=w.softmax_scale, out=o, lse=l, causal=causal)
         assert avf.async_status(ws) == 0
+        check_oracle(o, l, t, w)
         assert torch.equal(o, ref_o) and torch.equal(l, ref_l), max_k
 
 

@@ -93,6 +93,49 @@ def test_our_grid_is_exact_for_every_workload():
         assert launches == 1
 
 
+def test_num_tiles_is_the_exact_grid_of_a_call():
+    for w in WORKLOADS.values():
+        _, wgs = avf.grid_plan(w.cu_q, w.num_heads, w.head_dim, w.max_seqlen_k)
+        assert avf.num_tiles(w.cu_q, w.num_heads, w.head_dim, w.max_seqlen_k) == wgs
+    # the SM120 page's cu_seqlens_q at 56 heads: 15680 valid tiles at tile_m = 128,
+    # which a call with at most 512 keys per segment (128-row tiles) launches exactly
+    g = GOLDEN["varlen_grid"]
+    assert avf.block_m(128, 512) == g["tile_m"]
+    assert avf.num_tiles(g["cu_seqlens_q"], g["num_heads"], 128, 512) == g["valid_tiles"]
+    assert avf.num_tiles(g["cu_seqlens_q"], g["num_heads"], 128, 17580) == \
+        avf.count_tiles(g["cu_seqlens_q"], g["num_heads"], avf.block_m(128))
+    assert avf.num_tiles([0], 56, 128, 1000) == 0
+    for bad, code in (([1, 5], _binding.ECU), ([0, 5, 4], _binding.ECU)):
+        with pytest.raises(avf.AttnVarlenError) as e:
+            avf.num_tiles(bad, 2, 128, 100)
+        assert e.value.code == code
+    with pytest.raises(avf.AttnVarlenError):
+        avf.num_tiles([0, 5], 2, 80, 100)
+
+
+def test_oversized_segment_is_rejected_before_any_launch():
+    # The second segment alone needs 2^23 tiles (over the per-launch limit);
+    # the first is small. Every entry point must refuse the call before any
+    # HIP call, so no launch for the first segment (or fp8 quantization, or
+    # backward preprocessing) is left queued. Without a GPU here, a HIP call
+    # would have returned EHIP instead.
+    H, D, n = 8, 128, 1 << 28
+    cq = [0, 1, 1 + n]
+    lay = layout(H=H, D=D, nq=1 + n, nk=1 + n)
+    assert v(cu_q=cq, cu_k=cq, H=H, D=D, max_q=n, max_k=n, lay=lay) == _binding.EUNSUPPORTED
+    L = avf.lib()
+    c = (ctypes.c_int32 * 3)(*cq)
+    rc = L.attn_varlen_fwd_hostcu(P, P, P, c, c, 2, H, D, n, n, ctypes.byref(lay), 0.125, P, P, None)
+    assert rc == _binding.EUNSUPPORTED, avf.last_error()
+    big = 1 << 40
+    rc = L.attn_varlen_fwd_fp8_hostcu(P, P, P, c, c, 2, H, D, n, n, ctypes.byref(lay), 0.125, 0, P, big, P, P, None)
+    assert rc == _binding.EUNSUPPORTED, avf.last_error()
+    bl = bwd_layout(H=H, D=D, nq=1 + n, nk=1 + n)
+    rc = L.attn_varlen_bwd_hostcu(P, P, P, P, P, P, c, c, 2, H, D, n, n, ctypes.byref(bl), 0.125, 0, P, P, P, P,
+                                  None)
+    assert rc == _binding.EUNSUPPORTED, avf.last_error()
+
+
 def test_grid_plan_splits_long_segment_lists():
     spl = avf.segments_per_launch()
     rng = random.Random(0)
@@ -217,6 +260,7 @@ def test_validate_accepts_good_arguments():
     (dict(lay=layout(o_row=64, o_head=64)), _binding.EINVAL),      # out rows and heads alias
     (dict(lay=layout(o_row=120, o_head=64)), _binding.EINVAL),     # rows overlap within a head
     (dict(lay=layout(lse_head=8)), _binding.EINVAL),               # lse heads overlap
+    (dict(lay=layout(o_head=0)), _binding.EINVAL),                 # every head writes the same out elements
 ])
 def test_validate_rejects(kwargs, code):
     rc = v(**kwargs)
@@ -251,6 +295,11 @@ def test_forward_rejects_cpu_tensors_before_any_hip_call():
     cu = torch.tensor([0, 4], dtype=torch.int32)
     with pytest.raises(ValueError):
         avf.attn_varlen_fwd(q, q, q, cu, cu, 4, 4)
+    # the sync-free and 8-bit front ends check the same before marshalling
+    with pytest.raises(ValueError, match="device tensors"):
+        avf.attn_varlen_fwd_async(q, q, q, cu, cu, 4, 4, workspace=torch.zeros(64, dtype=torch.int32))
+    with pytest.raises(ValueError, match="device tensors"):
+        avf.attn_varlen_fwd_fp8(q, q, q, cu, cu, 4, 4, workspace=torch.zeros(1 << 12, dtype=torch.uint8))
 
 
 # ------------------------------------------------------------ option flags and the batched entry
@@ -301,11 +350,22 @@ def test_batched_validate_accepts():
     (dict(lay=blayout(o_batch=4 * 2 * 64)), _binding.EINVAL),       # out batches overlap
     (dict(lay=blayout(lse_batch=5)), _binding.EINVAL),              # lse batches overlap
     (dict(lay=blayout(lse_head=3)), _binding.EINVAL),               # lse heads overlap
+    (dict(lay=blayout(lse_head=0)), _binding.EINVAL),               # both heads write one lse row
+    (dict(lay=blayout(o_head=0)), _binding.EINVAL),                 # both heads write one out row
+    (dict(lay=blayout(lse_batch=0)), _binding.EINVAL),              # every batch writes one lse block
     (dict(W=1 << 20, Sq=1 << 12), _binding.EUNSUPPORTED),           # W * Sq >= 2^31
     (dict(D=80, lay=blayout(D=80)), _binding.EUNSUPPORTED),
 ])
 def test_batched_validate_rejects(kwargs, code):
     assert vb(**kwargs) == code
+
+
+def test_zero_strides_are_fine_where_the_extent_is_one():
+    # one head: its stride never matters (the LSE and out rows cannot collide)
+    assert vb(H=1, lay=blayout(H=1, lse_head=0, o_head=0)) == 0
+    assert v(H=1, lay=layout(H=1, o_head=0)) == 0
+    # one batch: the batch strides never matter
+    assert vb(W=1, lay=blayout(W=1, lse_batch=0, o_batch=0)) == 0
 
 
 # ---------------------------------------------------------------- backward (host checks only)
@@ -347,6 +407,9 @@ def test_bwd_validate_accepts():
     (dict(dq_row=0), _binding.EINVAL),
     (dict(dk_head=-8), _binding.EINVAL),
     (dict(dv_row=8, dv_head=8), _binding.EINVAL),            # dv rows overlap
+    (dict(dq_head=0), _binding.EINVAL),                      # both heads write one dq row
+    (dict(dk_head=0), _binding.EINVAL),
+    (dict(dv_head=0), _binding.EINVAL),
     (dict(delta_head=8), _binding.EINVAL),                   # delta rows of head 1 overlap head 0
     (dict(lse_head=4), _binding.EINVAL),
     (dict(do_row=1 << 23), _binding.EUNSUPPORTED),

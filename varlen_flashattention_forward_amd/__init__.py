@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     async_workspace_bytes, attn_fwd, attn_varlen_bwd, attn_varlen_fwd, attn_varlen_fwd_async, attn_varlen_fwd_fp8,
     fp8_workspace_bytes, fp8_workspace_offsets,
     block_m, bwd_grid_plan, bwd_preprocess, count_tiles, decode_tile, element_offset, grid_plan, last_error, lib,
+    num_tiles,
     one_stage_keys, short_stage_keys,
     segments_per_launch, validate, validate_batched, validate_bwd,
 )

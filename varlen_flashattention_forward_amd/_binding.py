@@ -31,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "attn_varlen_async_status", "attn_varlen_async_grid", "attn_varlen_fp8_workspace_bytes",
     "attn_varlen_fp8_workspace_offsets", "attn_varlen_fwd_fp8", "attn_varlen_fwd_fp8_hostcu",
     "attn_varlen_block_m_for", "attn_varlen_one_stage_keys", "attn_varlen_short_stage_keys",
+    "attn_varlen_num_tiles",
 )
 
 CAUSAL = 1  # ATTN_VARLEN_CAUSAL
@@ -138,6 +139,9 @@ def lib():
         L.attn_varlen_short_stage_keys.argtypes = []
         L.attn_varlen_count_tiles.restype = ctypes.c_int64
         L.attn_varlen_count_tiles.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+        L.attn_varlen_num_tiles.restype = ctypes.c_int64
+        L.attn_varlen_num_tiles.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32]
         L.attn_varlen_grid_plan.restype = ctypes.c_int32
         L.attn_varlen_grid_plan.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             _i64p, _i64p]
@@ -194,6 +198,16 @@ def short_stage_keys() -> int:
 def count_tiles(cu_q, num_heads: int, block_m_: int) -> int:
     arr, B = _cu_array(cu_q)
     r = lib().attn_varlen_count_tiles(arr, B, num_heads, block_m_)
+    if r < 0:
+        _check(int(r))
+    return int(r)
+
+
+def num_tiles(cu_q, num_heads: int, head_dim: int, max_seqlen_k: int) -> int:
+    """Exact workgroup total of one attn_varlen_fwd call with these host
+    cu_seqlens_q, head count, head_dim and max_seqlen_k."""
+    arr, B = _cu_array(cu_q)
+    r = lib().attn_varlen_num_tiles(arr, B, num_heads, head_dim, max_seqlen_k)
     if r < 0:
         _check(int(r))
     return int(r)
@@ -256,6 +270,35 @@ def _layout_of(q, k, v, out, lse, lse_head):
                   out.stride(0), out.stride(1), lse_head, q.shape[0], k.shape[0])
 
 
+def _fwd_tensors(q, k, v, out, lse, return_lse: bool):
+    """Check the forward's q, k, v (and a caller-supplied out / lse) and
+    allocate what is missing. Returns (total_q, H, D, out, lse, lse_head)."""
+    import torch
+
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [total_q, H, D] and k, v [total_k, H, D]")
+    total_q, H, D = q.shape
+    if k.shape[1:] != (H, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [total_k, H, D] matching q's H and D")
+    if out is None:
+        out = torch.empty((total_q, H, D), dtype=torch.bfloat16, device=q.device)
+    elif out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_cuda or out.device != q.device:
+        raise ValueError("out must be a bf16 device tensor with q's shape on q's device")
+    lse_head = 0
+    if lse is None and return_lse:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        if lse.dtype != torch.float32 or lse.dim() != 2 or lse.shape[0] != H or lse.stride(1) != 1 \
+                or lse.shape[1] < total_q or not lse.is_cuda or lse.device != q.device:
+            raise ValueError("lse must be an fp32 device tensor [H, >= total_q] with unit inner stride")
+        lse_head = lse.stride(0)
+    return total_q, H, D, out, lse, lse_head
+
+
 def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                     softmax_scale: float | None = None, out=None, lse=None, return_lse: bool = True,
                     cu_seqlens_q_host=None, cu_seqlens_k_host=None, stream=None, causal: bool = False):
@@ -269,27 +312,9 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
     """
     import torch
 
-    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
-        raise TypeError("q, k, v must be bfloat16")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
-        raise ValueError("q, k, v must be device tensors")
-    total_q, H, D = q.shape
-    if k.shape[1:] != (H, D) or v.shape != k.shape:
-        raise ValueError("k and v must be [total_k, H, D] matching q's H and D")
+    total_q, H, D, out, lse, lse_head = _fwd_tensors(q, k, v, out, lse, return_lse)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((total_q, H, D), dtype=torch.bfloat16, device=q.device)
-    elif out.dtype != torch.bfloat16 or out.shape != q.shape:
-        raise ValueError("out must be bf16 with q's shape")
-    lse_head = 0
-    if lse is None and return_lse:
-        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        if lse.dtype != torch.float32 or lse.dim() != 2 or lse.shape[0] != H or lse.stride(1) != 1 \
-                or lse.shape[1] < total_q:
-            raise ValueError("lse must be fp32 [H, >= total_q] with unit inner stride")
-        lse_head = lse.stride(0)
     layout = _layout_of(q, k, v, out, lse, lse_head)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -364,11 +389,7 @@ def attn_varlen_fwd_async(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int
     """
     import torch
 
-    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
-        raise TypeError("q, k, v must be bfloat16")
-    total_q, H, D = q.shape
-    if k.shape[1:] != (H, D) or v.shape != k.shape:
-        raise ValueError("k and v must be [total_k, H, D] matching q's H and D")
+    total_q, H, D, out, lse, lse_head = _fwd_tensors(q, k, v, out, lse, return_lse)
     for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
         if cu.dtype != torch.int32 or not cu.is_cuda or cu.dim() != 1 or not cu.is_contiguous():
             raise ValueError(f"{name} must be a contiguous int32 device tensor")
@@ -377,18 +398,10 @@ def attn_varlen_fwd_async(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int
         raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((total_q, H, D), dtype=torch.bfloat16, device=q.device)
-    lse_head = 0
-    if lse is None and return_lse:
-        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        if lse.dtype != torch.float32 or lse.dim() != 2 or lse.shape[0] != H or lse.stride(1) != 1 \
-                or lse.shape[1] < total_q:
-            raise ValueError("lse must be fp32 [H, >= total_q] with unit inner stride")
-        lse_head = lse.stride(0)
     if workspace is None:
         workspace = async_workspace(B, q.device)
+    elif not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor on q's device")
     layout = _layout_of(q, k, v, out, lse, lse_head)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -426,25 +439,13 @@ def attn_varlen_fwd_fp8(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, 
     Returns (out, lse, workspace)."""
     import torch
 
-    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
-        raise TypeError("q, k, v must be bfloat16")
-    total_q, H, D = q.shape
-    if k.shape[1:] != (H, D) or v.shape != k.shape:
-        raise ValueError("k and v must be [total_k, H, D] matching q's H and D")
+    total_q, H, D, out, lse, lse_head = _fwd_tensors(q, k, v, out, lse, return_lse)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((total_q, H, D), dtype=torch.bfloat16, device=q.device)
-    lse_head = 0
-    if lse is None and return_lse:
-        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        if lse.dtype != torch.float32 or lse.dim() != 2 or lse.shape[0] != H or lse.stride(1) != 1 \
-                or lse.shape[1] < total_q:
-            raise ValueError("lse must be fp32 [H, >= total_q] with unit inner stride")
-        lse_head = lse.stride(0)
     if workspace is None:
         workspace = torch.empty(fp8_workspace_bytes(total_q, k.shape[0], H, D), dtype=torch.uint8, device=q.device)
+    elif not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor on q's device")
     layout = _layout_of(q, k, v, out, lse, lse_head)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -547,8 +548,9 @@ def validate_bwd(ptrs, cu_q, cu_k, num_heads, head_dim, max_q, max_k, layout: Bw
 def _fp32_rows(t, name, H, total_q):
     import torch
 
-    if t.dtype != torch.float32 or t.dim() != 2 or t.shape[0] != H or t.stride(1) != 1 or t.shape[1] < total_q:
-        raise ValueError(f"{name} must be fp32 [H, >= total_q] with unit inner stride")
+    if t.dtype != torch.float32 or t.dim() != 2 or t.shape[0] != H or t.stride(1) != 1 or t.shape[1] < total_q \
+            or not t.is_cuda:
+        raise ValueError(f"{name} must be an fp32 device tensor [H, >= total_q] with unit inner stride")
     return t.stride(0)
 
 
@@ -599,7 +601,7 @@ def attn_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        if t.dtype != torch.bfloat16 or t.shape != ref.shape or t.stride(2) != 1:
+        if t.dtype != torch.bfloat16 or t.shape != ref.shape or t.stride(2) != 1 or not t.is_cuda:
             raise ValueError(f"{name} must be bf16 with {('q', 'k', 'v')[('dq', 'dk', 'dv').index(name)]}'s shape")
     if delta is None:
         delta = torch.empty((H, total_q), dtype=torch.float32, device=q.device)

@@ -35,12 +35,19 @@ int32_t fail(int32_t code, const char* fmt, ...) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // (extent, stride) pairs of a tensor: true if no two elements share an
-// address (each stride, in increasing order, spans everything below it).
+// address (each stride, in increasing order, spans everything below it). A
+// tensor without elements never overlaps; otherwise a dimension of extent > 1
+// with a stride below 1 (0 repeats one address) always does.
 struct Dim { int64_t extent, stride; };
 bool non_overlapping_dims(std::vector<Dim> in) {
-    std::vector<Dim> dims;
     for (const Dim& x : in)
-        if (x.extent > 1) dims.push_back(x);
+        if (x.extent <= 0) return true;
+    std::vector<Dim> dims;
+    for (const Dim& x : in) {
+        if (x.extent <= 1) continue;
+        if (x.stride < 1) return false;
+        dims.push_back(x);
+    }
     std::sort(dims.begin(), dims.end(), [](const Dim& x, const Dim& y) { return x.stride < y.stride; });
     for (size_t i = 1; i < dims.size(); ++i) {
         const __int128 span = (__int128)dims[i - 1].extent * dims[i - 1].stride;
@@ -201,6 +208,20 @@ int64_t fill_plan(AvfLaunchArgs& a, const int32_t* cu_q, const int32_t* cu_k, in
 // kernel uses, 512 threads (the forward's eight waves).
 constexpr int64_t kMaxTilesPerLaunch = ((int64_t)1 << 32) / 512 - 1;
 
+// Every segment of `tiled` (cut into blocks of `bm` rows, times H heads) must
+// fit one launch. Checked over all segments before the first HIP call of an
+// entry point, so a segment that is too large never leaves earlier launches
+// (or the fp8 quantization, or the backward's preprocessing) queued.
+int32_t check_launch_limits(const int32_t* tiled, int32_t B, int32_t H, int32_t bm) {
+    for (int32_t b = 0; b < B; ++b) {
+        const int64_t tb = tiles_of(tiled, b, b + 1, H, bm);
+        if (tb > kMaxTilesPerLaunch)
+            return fail(ATTN_VARLEN_EUNSUPPORTED, "segment %d needs %lld tiles (limit %lld per launch)", b,
+                        (long long)tb, (long long)kMaxTilesPerLaunch);
+    }
+    return ATTN_VARLEN_OK;
+}
+
 // Forward configuration from the call's max_seqlen_k (which bounds every key
 // segment: checked against cu_seqlens on the host, or by the device planner):
 // one-stage (one 128-key K/V stage), short-stage (64-key stages), or the
@@ -241,16 +262,16 @@ int32_t run(const void* q, const void* k, const void* v, const int32_t* cu_q, co
     a.q8 = q8; a.k8 = k8; a.amax8 = amax8;
     a.one_stage = cfg == FwdCfg::one_stage;
     a.short_stage = cfg == FwdCfg::short_stage;
+    const int32_t rc = check_launch_limits(cu_q, B, H, bm);
+    if (rc != ATTN_VARLEN_OK) return rc;
     for (int32_t b0 = 0; b0 < B;) {
-        // segments of this launch: at most AVF_SEGS_PER_LAUNCH and at most kMaxTilesPerLaunch tiles
+        // segments of this launch: at most AVF_SEGS_PER_LAUNCH and at most
+        // kMaxTilesPerLaunch tiles (every single segment fits: checked above)
         int32_t b1 = b0;
         int64_t t = 0;
         while (b1 < B && b1 - b0 < AVF_SEGS_PER_LAUNCH) {
             const int64_t tb = tiles_of(cu_q, b1, b1 + 1, H, bm);
             if (t + tb > kMaxTilesPerLaunch && b1 > b0) break;
-            if (tb > kMaxTilesPerLaunch)
-                return fail(ATTN_VARLEN_EUNSUPPORTED, "segment %d needs %lld tiles (limit %lld per launch)",
-                            b1, (long long)tb, (long long)kMaxTilesPerLaunch);
             t += tb;
             ++b1;
         }
@@ -275,9 +296,11 @@ int32_t attn_varlen_validate_ex(const void* q, const void* k, const void* v, con
                                 int32_t max_k, const attn_varlen_layout* st, float scale,
                                 uint32_t flags, const void* out, const float* lse) {
     g_last_error.clear();
-    const int32_t rc = check_flags(flags);
+    int32_t rc = check_flags(flags);
     if (rc != ATTN_VARLEN_OK) return rc;
-    return validate_all(q, k, v, cu_q, cu_k, B, H, D, max_q, max_k, st, scale, out, lse);
+    rc = validate_all(q, k, v, cu_q, cu_k, B, H, D, max_q, max_k, st, scale, out, lse);
+    if (rc != ATTN_VARLEN_OK || B == 0) return rc;
+    return check_launch_limits(cu_q, B, H, fwd_block_m(D, fwd_config(max_k, false)));
 }
 
 int32_t attn_varlen_validate(const void* q, const void* k, const void* v, const int32_t* cu_q,
@@ -474,6 +497,18 @@ int32_t attn_varlen_grid_plan(const int32_t* cu_q, int32_t B, int32_t H, int32_t
     *launches = nl;
     *workgroups = nw;
     return ATTN_VARLEN_OK;
+}
+
+int64_t attn_varlen_num_tiles(const int32_t* cu_q, int32_t B, int32_t H, int32_t D, int32_t max_k) {
+    g_last_error.clear();
+    if (!cu_q) return fail(ATTN_VARLEN_ENULL, "cu_seqlens_q is NULL");
+    if (B < 0 || H <= 0) return fail(ATTN_VARLEN_EINVAL, "bad counts");
+    if (B > 0 && cu_q[0] != 0) return fail(ATTN_VARLEN_ECU, "cu_seqlens_q must start at 0");
+    for (int32_t b = 0; b < B; ++b)
+        if (cu_q[b + 1] < cu_q[b]) return fail(ATTN_VARLEN_ECU, "cu_seqlens_q decreases at %d", b);
+    int64_t launches = 0, workgroups = 0;
+    const int32_t rc = attn_varlen_grid_plan(cu_q, B, H, D, max_k, &launches, &workgroups);
+    return rc != ATTN_VARLEN_OK ? rc : workgroups;
 }
 
 int32_t attn_varlen_decode_tile(const int32_t* cu_q, int32_t B, int32_t H, int32_t block_m,
@@ -673,12 +708,15 @@ int32_t bwd_run(const void* q, const void* k, const void* v, const void* o, cons
                 const int32_t* cu_q, const int32_t* cu_k, int32_t B, int32_t H, int32_t D,
                 const attn_varlen_bwd_layout* st, float scale, uint32_t flags, float* delta, void* dq, void* dk,
                 void* dv, hipStream_t s) {
+    int32_t rc = check_launch_limits(cu_k, B, H, avf_bwd_block_n(D));
+    if (rc == ATTN_VARLEN_OK) rc = check_launch_limits(cu_q, B, H, avf_bwd_block_m(D));
+    if (rc != ATTN_VARLEN_OK) return rc;
     const int64_t delta_head = st->delta_head ? st->delta_head : st->q_tokens;
     hipError_t e = preprocess(o, g, cu_q[B], H, D, st->o_row, st->o_head, st->do_row, st->do_head, delta,
                               delta_head, s);
     if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "preprocessing launch failed: %s", hipGetErrorString(e));
     AvfBwdArgs a = bwd_args(q, k, v, g, lse, delta, dq, dk, dv, H, st, scale, flags);
-    int32_t rc = for_each_launch(a, cu_q, cu_k, cu_k, B, H, avf_bwd_block_n(D),
+    rc = for_each_launch(a, cu_q, cu_k, cu_k, B, H, avf_bwd_block_n(D),
                                  [&](const AvfBwdArgs& x) { return avf_bwd_dkdv_launch(x, D, s); }, nullptr, nullptr);
     if (rc != ATTN_VARLEN_OK) return rc;
     return for_each_launch(a, cu_q, cu_k, cu_q, B, H, avf_bwd_block_m(D),
@@ -923,6 +961,8 @@ int32_t fp8_run(const void* q, const void* k, const void* v, const int32_t* cu_q
     if (workspace_bytes < l.bytes)
         return fail(ATTN_VARLEN_EINVAL, "workspace of %lld bytes is smaller than the %lld needed",
                     (long long)workspace_bytes, (long long)l.bytes);
+    const int32_t rc = check_launch_limits(cu_q, B, H, fwd_block_m(D, FwdCfg::general));
+    if (rc != ATTN_VARLEN_OK) return rc;
     char* ws = static_cast<char*>(workspace);
     AvfQuantArgs qa;
     qa.q = q; qa.k = k;
