@@ -347,6 +347,36 @@ int32_t attn_varlen_fwd_async(const void* q, const void* k, const void* v,
                               void* workspace, int64_t workspace_bytes, void* out, float* lse,
                               void* stream);
 
+/*
+ * attn_varlen_fwd_async for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The caller passes inputs and outputs only; the plan and status
+ * words that attn_varlen_fwd_async keeps in the caller's workspace live in a
+ * static device array of the library instead (about 256 KiB, one copy per
+ * GPU, held until the process ends), whose device address is looked up once
+ * per GPU on the first call with that GPU current. The call allocates
+ * nothing (no hipMalloc, no library allocation).
+ *   num_segments  at most 65536 (the static plan's size); more is
+ *                 ATTN_VARLEN_EUNSUPPORTED, returned before any HIP call.
+ *   plan          if non-NULL, receives the device address of this GPU's
+ *                 static plan (NULL when nothing was enqueued, e.g. B == 0);
+ *                 pass it to attn_varlen_async_status to read the call's
+ *                 status word once `stream` has reached it.
+ * Every call on one GPU uses that GPU's single static plan, and each call's
+ * planner rewrites every plan word the call reads (nothing needs clearing).
+ * Calls that overlap on one GPU (on different streams, or from different
+ * threads without ordering) race on the plan and must not be issued; calls
+ * ordered on one stream are safe. Other arguments, results and errors as in
+ * attn_varlen_fwd_async.
+ */
+int32_t attn_varlen_fwd_async_noalloc(const void* q, const void* k, const void* v,
+                                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                      int32_t num_segments, int32_t num_heads, int32_t head_dim,
+                                      int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                      const attn_varlen_layout* layout, float softmax_scale,
+                                      uint32_t flags, void* out, float* lse, void* stream,
+                                      const void** plan);
+
 /* Copy the workspace's status word to *status (waits for `stream`). */
 int32_t attn_varlen_async_status(const void* workspace, void* stream, int32_t* status);
 

@@ -7,7 +7,8 @@ package is the thin Python binding over it.
 """
 from ._binding import (  # noqa: F401
     CAUSAL, AttnVarlenError, BatchedLayout, BwdLayout, Layout, async_grid, async_status, async_workspace,
-    async_workspace_bytes, attn_fwd, attn_varlen_bwd, attn_varlen_fwd, attn_varlen_fwd_async, attn_varlen_fwd_fp8,
+    async_workspace_bytes, attn_fwd, attn_varlen_bwd, attn_varlen_fwd, attn_varlen_fwd_async, attn_varlen_fwd_async_noalloc,
+    attn_varlen_fwd_fp8,
     fp8_workspace_bytes, fp8_workspace_offsets,
     block_m, bwd_grid_plan, bwd_preprocess, count_tiles, decode_tile, element_offset, grid_plan, last_error, lib,
     num_tiles,

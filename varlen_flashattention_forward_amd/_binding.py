@@ -31,7 +31,7 @@ EXPORTED_SYMBOLS = (
     "attn_varlen_async_status", "attn_varlen_async_grid", "attn_varlen_fp8_workspace_bytes",
     "attn_varlen_fp8_workspace_offsets", "attn_varlen_fwd_fp8", "attn_varlen_fwd_fp8_hostcu",
     "attn_varlen_block_m_for", "attn_varlen_one_stage_keys", "attn_varlen_short_stage_keys",
-    "attn_varlen_num_tiles",
+    "attn_varlen_num_tiles", "attn_varlen_fwd_async_noalloc",
 )
 
 CAUSAL = 1  # ATTN_VARLEN_CAUSAL
@@ -116,6 +116,9 @@ def lib():
         L.attn_varlen_async_workspace_bytes.argtypes = [ctypes.c_int32]
         L.attn_varlen_fwd_async.restype = ctypes.c_int32
         L.attn_varlen_fwd_async.argtypes = fwd_args[:12] + [ctypes.c_uint32, _vp, ctypes.c_int64] + fwd_args[12:]
+        L.attn_varlen_fwd_async_noalloc.restype = ctypes.c_int32
+        L.attn_varlen_fwd_async_noalloc.argtypes = fwd_args[:12] + [ctypes.c_uint32] + fwd_args[12:] + \
+            [ctypes.POINTER(ctypes.c_void_p)]
         L.attn_varlen_async_status.restype = ctypes.c_int32
         L.attn_varlen_async_status.argtypes = [_vp, _vp, _i32p]
         L.attn_varlen_async_grid.restype = ctypes.c_int32
@@ -367,13 +370,19 @@ def async_workspace(num_segments: int, device):
 
 
 def async_status(workspace, stream=None) -> int:
-    """The planner's status word of the last call that used `workspace` (waits for the stream)."""
+    """The planner's status word of the last call that used `workspace` (waits
+    for the stream). `workspace` is a workspace tensor, or the integer plan
+    address that attn_varlen_fwd_async_noalloc returns (current device)."""
     import torch
 
+    if isinstance(workspace, int):
+        ptr, dev = workspace, torch.device("cuda", torch.cuda.current_device())
+    else:
+        ptr, dev = workspace.data_ptr(), workspace.device
     if stream is None:
-        stream = torch.cuda.current_stream(workspace.device).cuda_stream
+        stream = torch.cuda.current_stream(dev).cuda_stream
     st = ctypes.c_int32()
-    _check(lib().attn_varlen_async_status(workspace.data_ptr(), stream, ctypes.byref(st)))
+    _check(lib().attn_varlen_async_status(ptr, stream, ctypes.byref(st)))
     return st.value
 
 
@@ -412,6 +421,40 @@ def attn_varlen_fwd_async(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int
                                      out.data_ptr(), lse.data_ptr() if lse is not None else None, stream)
     _check(rc)
     return out, lse, workspace
+
+
+def attn_varlen_fwd_async_noalloc(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                                  softmax_scale: float | None = None, out=None, lse=None, return_lse: bool = True,
+                                  stream=None, causal: bool = False):
+    """attn_varlen_fwd_async with the plan in the library's static device
+    array instead of a workspace (the C entry point allocates nothing; pass
+    out and lse to allocate nothing here either). At most 65536 segments.
+    Returns (out, lse, plan): plan is the integer device address of the
+    static plan for async_status, or None when nothing was enqueued."""
+    import torch
+
+    total_q, H, D, out, lse, lse_head = _fwd_tensors(q, k, v, out, lse, return_lse)
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if cu.dtype != torch.int32 or not cu.is_cuda or cu.dim() != 1 or not cu.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    B = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    layout = _layout_of(q, k, v, out, lse, lse_head)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    plan = ctypes.c_void_p()
+    with torch.cuda.device(q.device):
+        rc = lib().attn_varlen_fwd_async_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
+                                                 cu_seqlens_k.data_ptr(), B, H, D, int(max_seqlen_q),
+                                                 int(max_seqlen_k), ctypes.byref(layout), float(softmax_scale),
+                                                 CAUSAL if causal else 0, out.data_ptr(),
+                                                 lse.data_ptr() if lse is not None else None, stream,
+                                                 ctypes.byref(plan))
+    _check(rc)
+    return out, lse, plan.value
 
 
 def fp8_workspace_bytes(total_q: int, total_k: int, num_heads: int, head_dim: int) -> int:

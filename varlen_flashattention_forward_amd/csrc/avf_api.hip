@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <climits>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -843,42 +844,16 @@ int64_t async_grid(int64_t bound) {
     return (g + AVF_NUM_XCD - 1) / AVF_NUM_XCD * AVF_NUM_XCD;
 }
 
-}  // namespace
-
-extern "C" {
-
-int64_t attn_varlen_async_workspace_bytes(int32_t B) {
-    g_last_error.clear();
-    if (B < 0) return fail(ATTN_VARLEN_EINVAL, "num_segments must be >= 0 (got %d)", B);
-    return async_workspace_bytes(B);
-}
-
-int32_t attn_varlen_async_grid(int64_t q_tokens, int32_t B, int32_t H, int32_t D, int32_t max_q, int32_t max_k,
-                               int64_t* workgroups) {
-    g_last_error.clear();
-    if (!workgroups) return fail(ATTN_VARLEN_ENULL, "NULL argument");
-    if (B < 0 || H <= 0 || q_tokens < 0 || max_q < 0 || max_k < 0) return fail(ATTN_VARLEN_EINVAL, "bad counts");
-    const int32_t bm = fwd_block_m(D, fwd_config(max_k, false));
-    if (bm <= 0) return fail(ATTN_VARLEN_EUNSUPPORTED, "head_dim %d not supported", D);
-    *workgroups = async_grid(async_tile_bound(q_tokens, B, H, bm, max_q));
-    return ATTN_VARLEN_OK;
-}
-
-int32_t attn_varlen_fwd_async(const void* q, const void* k, const void* v, const int32_t* cu_q_dev,
-                              const int32_t* cu_k_dev, int32_t B, int32_t H, int32_t D, int32_t max_q,
-                              int32_t max_k, const attn_varlen_layout* st, float scale, uint32_t flags,
-                              void* workspace, int64_t workspace_bytes, void* out, float* lse, void* stream) {
-    g_last_error.clear();
+// Host-side checks of the sync-free forward (every value the host knows; the
+// cu values are checked by the planner on the device).
+int32_t async_check(const void* q, const void* k, const void* v, const int32_t* cu_q_dev, const int32_t* cu_k_dev,
+                    int32_t B, int32_t H, int32_t D, int32_t max_q, int32_t max_k, const attn_varlen_layout* st,
+                    float scale, uint32_t flags, const void* out, const float* lse) {
     int32_t rc = check_flags(flags);
     if (rc != ATTN_VARLEN_OK) return rc;
     rc = check_scalars(q, k, v, B, H, D, max_q, max_k, st, scale, out, lse);
     if (rc != ATTN_VARLEN_OK || B == 0) return rc;
     if (!cu_q_dev || !cu_k_dev) return fail(ATTN_VARLEN_ENULL, "cu_seqlens_q/k must be non-NULL");
-    if (!workspace) return fail(ATTN_VARLEN_ENULL, "workspace must be non-NULL");
-    if (reinterpret_cast<uintptr_t>(workspace) & 15u) return fail(ATTN_VARLEN_EALIGN, "workspace must be 16-byte aligned");
-    if (workspace_bytes < async_workspace_bytes(B))
-        return fail(ATTN_VARLEN_EINVAL, "workspace of %lld bytes is smaller than the %lld needed",
-                    (long long)workspace_bytes, (long long)async_workspace_bytes(B));
     // the checks that need cu, with q_tokens standing in for the unknown total_q
     if (!non_overlapping(st->q_tokens, st->o_row, H, st->o_head, D))
         return fail(ATTN_VARLEN_EINVAL, "out strides (row %lld, head %lld) make elements overlap",
@@ -886,11 +861,18 @@ int32_t attn_varlen_fwd_async(const void* q, const void* k, const void* v, const
     if (lse && H > 1 && st->lse_head != 0 && st->lse_head < st->q_tokens)
         return fail(ATTN_VARLEN_EINVAL, "lse_head %lld is smaller than q_tokens %lld", (long long)st->lse_head,
                     (long long)st->q_tokens);
+    return ATTN_VARLEN_OK;
+}
+
+// The planner kernel into `ws` (a plan buffer of at least
+// async_workspace_bytes(B) bytes), then the attention kernel on the host
+// bound of the tile count, both on stream `s`.
+int32_t async_launch(const void* q, const void* k, const void* v, const int32_t* cu_q_dev, const int32_t* cu_k_dev,
+                     int32_t B, int32_t H, int32_t D, int32_t max_q, int32_t max_k, const attn_varlen_layout* st,
+                     float scale, uint32_t flags, int32_t* ws, void* out, float* lse, hipStream_t s) {
     // the planner rejects any segment over max_k, so max_k may pick the one-stage configuration
     const FwdCfg cfg = fwd_config(max_k, false);
     const int32_t bm = fwd_block_m(D, cfg);
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    int32_t* ws = static_cast<int32_t*>(workspace);
     hipError_t e = avf_plan_launch(cu_q_dev, cu_k_dev, B, H, bm, 0, max_q, max_k, st->q_tokens, st->k_tokens, ws, s);
     if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "planner launch failed: %s", hipGetErrorString(e));
     const int64_t grid = async_grid(async_tile_bound(st->q_tokens, B, H, bm, max_q));
@@ -917,6 +899,115 @@ int32_t attn_varlen_fwd_async(const void* q, const void* k, const void* v, const
     e = avf_launch(a, D, s);
     if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ATTN_VARLEN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t attn_varlen_async_workspace_bytes(int32_t B) {
+    g_last_error.clear();
+    if (B < 0) return fail(ATTN_VARLEN_EINVAL, "num_segments must be >= 0 (got %d)", B);
+    return async_workspace_bytes(B);
+}
+
+int32_t attn_varlen_async_grid(int64_t q_tokens, int32_t B, int32_t H, int32_t D, int32_t max_q, int32_t max_k,
+                               int64_t* workgroups) {
+    g_last_error.clear();
+    if (!workgroups) return fail(ATTN_VARLEN_ENULL, "NULL argument");
+    if (B < 0 || H <= 0 || q_tokens < 0 || max_q < 0 || max_k < 0) return fail(ATTN_VARLEN_EINVAL, "bad counts");
+    const int32_t bm = fwd_block_m(D, fwd_config(max_k, false));
+    if (bm <= 0) return fail(ATTN_VARLEN_EUNSUPPORTED, "head_dim %d not supported", D);
+    *workgroups = async_grid(async_tile_bound(q_tokens, B, H, bm, max_q));
+    return ATTN_VARLEN_OK;
+}
+
+int32_t attn_varlen_fwd_async(const void* q, const void* k, const void* v, const int32_t* cu_q_dev,
+                              const int32_t* cu_k_dev, int32_t B, int32_t H, int32_t D, int32_t max_q,
+                              int32_t max_k, const attn_varlen_layout* st, float scale, uint32_t flags,
+                              void* workspace, int64_t workspace_bytes, void* out, float* lse, void* stream) {
+    g_last_error.clear();
+    const int32_t rc = async_check(q, k, v, cu_q_dev, cu_k_dev, B, H, D, max_q, max_k, st, scale, flags, out, lse);
+    if (rc != ATTN_VARLEN_OK || B == 0) return rc;
+    if (!workspace) return fail(ATTN_VARLEN_ENULL, "workspace must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 15u) return fail(ATTN_VARLEN_EALIGN, "workspace must be 16-byte aligned");
+    if (workspace_bytes < async_workspace_bytes(B))
+        return fail(ATTN_VARLEN_EINVAL, "workspace of %lld bytes is smaller than the %lld needed",
+                    (long long)workspace_bytes, (long long)async_workspace_bytes(B));
+    return async_launch(q, k, v, cu_q_dev, cu_k_dev, B, H, D, max_q, max_k, st, scale, flags,
+                        static_cast<int32_t*>(workspace), out, lse, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Sync-free forward without any allocation: the plan lives in a static
+// device array of the library, one copy per GPU.
+
+namespace {
+
+// Largest segment count of one call of the no-allocation entry point; the
+// plan needs AVF_PLAN_HEADER_WORDS + B + 1 words.
+constexpr int32_t kNoAllocMaxSegments = 65536;
+constexpr int64_t kScratchWords = ((int64_t)AVF_PLAN_HEADER_WORDS + kNoAllocMaxSegments + 1 + 63) / 64 * 64;
+static_assert(kScratchWords * 4 >= 4 * ((int64_t)AVF_PLAN_HEADER_WORDS + kNoAllocMaxSegments + 1),
+              "the static plan holds the largest accepted call");
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+// The plan buffer of attn_varlen_fwd_async_noalloc (about 256 KiB). Each GPU
+// the library runs on holds its own copy until the process ends. In host
+// code this name only stands in for the device array: its device address,
+// per GPU, comes from hipGetSymbolAddress and is the only way host code
+// refers to it.
+static __device__ __align__(256) int32_t scratch[kScratchWords];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+int32_t* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each GPU
+
+// Device address of `scratch` on the current GPU, looked up once per GPU
+// (with that GPU current) and kept.
+int32_t scratch_on_current_device(int32_t** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_VARLEN_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(ATTN_VARLEN_EUNSUPPORTED, "device %d is past the %d GPUs the static plan serves", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(ATTN_VARLEN_EHIP, "hipGetSymbolAddress of the static plan failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+    }
+    *ptr = g_scratch_ptr[dev];
+    return ATTN_VARLEN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t attn_varlen_fwd_async_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_q_dev,
+                                      const int32_t* cu_k_dev, int32_t B, int32_t H, int32_t D, int32_t max_q,
+                                      int32_t max_k, const attn_varlen_layout* st, float scale, uint32_t flags,
+                                      void* out, float* lse, void* stream, const void** plan) {
+    g_last_error.clear();
+    if (plan) *plan = nullptr;
+    int32_t rc = async_check(q, k, v, cu_q_dev, cu_k_dev, B, H, D, max_q, max_k, st, scale, flags, out, lse);
+    if (rc != ATTN_VARLEN_OK || B == 0) return rc;
+    if (B > kNoAllocMaxSegments)
+        return fail(ATTN_VARLEN_EUNSUPPORTED, "num_segments %d exceeds the static plan's limit of %d segments", B,
+                    kNoAllocMaxSegments);
+    int32_t* ws = nullptr;
+    if ((rc = scratch_on_current_device(&ws)) != ATTN_VARLEN_OK) return rc;
+    if (plan) *plan = ws;
+    return async_launch(q, k, v, cu_q_dev, cu_k_dev, B, H, D, max_q, max_k, st, scale, flags, ws, out, lse,
+                        static_cast<hipStream_t>(stream));
 }
 
 int32_t attn_varlen_async_status(const void* workspace, void* stream, int32_t* status) {
