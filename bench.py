@@ -239,6 +239,63 @@ def bench_backward(args) -> int:
     return 0
 
 
+def bench_mfma_rate(args, dev) -> int:
+    """The rate a plain bf16 MFMA stream reaches on this GPU with the given
+    operand values (the calibration kernel of libavf_probe.so): under the
+    board's power limit the clock, and so the rate, depends on the operands'
+    switching activity. Random N(0,1) bf16 operands, like the attention
+    workloads' inputs, give the ceiling an MFMA-bound kernel on such data can
+    approach; all-ones operands show the clock with little switching."""
+    import ctypes
+
+    import torch
+
+    from varlen_flashattention_forward_amd import build as avf_build
+
+    if not avf_build.PROBE_LIB.exists():
+        raise RuntimeError(f"{avf_build.PROBE_LIB} is missing: build with python -m varlen_flashattention_forward_amd.build")
+    P = ctypes.CDLL(str(avf_build.PROBE_LIB))
+    P.avf_probe_operand_bytes.restype = ctypes.c_int64
+    P.avf_probe_operand_bytes.argtypes = [ctypes.c_int32]
+    P.avf_probe_output_bytes.restype = ctypes.c_int64
+    P.avf_probe_output_bytes.argtypes = [ctypes.c_int32]
+    P.avf_probe_mfma.restype = ctypes.c_int32
+    P.avf_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    wgs = 2 * cus            # 256-thread workgroups, two per CU: two waves per SIMD
+    iters = 400000           # about 0.1 s per launch
+    n = P.avf_probe_operand_bytes(wgs) // 2
+    g = torch.Generator(device=dev).manual_seed(0)
+    ops = (torch.randn(n, dtype=torch.bfloat16, device=dev, generator=g) if args.mfma_rate == "random"
+           else torch.ones(n, dtype=torch.bfloat16, device=dev))
+    out = torch.empty(P.avf_probe_output_bytes(wgs) // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def launch():
+        rc = P.avf_probe_mfma(ops.data_ptr(), out.data_ptr(), wgs, iters, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"avf_probe_mfma returned {rc}")
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = wgs * 4 * iters * 8 * 32768
+    tf = flops / (ms / 1e3) / 1e12
+    print(json.dumps({"metric": "bf16 MFMA rate of a plain v_mfma_f32_32x32x16_bf16 stream", "value": round(tf, 1),
+                      "unit": "TFLOP/s", "operands": "N(0,1) random bf16" if args.mfma_rate == "random" else "all ones",
+                      "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "peak": PEAK_BF16_TFLOPS,
+                      "ms_per_launch": round(ms, 3), "workgroups": wgs, "iters": iters, "compute_units": cus,
+                      "steps": args.steps, "warmup": args.warmup}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -259,6 +316,9 @@ def main() -> int:
                     help="only run a plain device-to-device copy of MIB MiB three times (scales HBM counters)")
     ap.add_argument("--head-major", action="store_true",
                     help="the workload's q, k, v and out as head-major views (row stride D, head stride tokens*D)")
+    ap.add_argument("--mfma-rate", choices=["random", "ones"], default=None,
+                    help="only time the roofline calibration kernel: a plain stream of bf16 MFMAs "
+                         "(v_mfma_f32_32x32x16_bf16) on N(0,1) random or all-ones bf16 operands, two waves per SIMD")
     ap.add_argument("--copy-rate", type=int, default=0, metavar="MIB",
                     help="only time a plain device-to-device copy of MIB MiB (--warmup, then --steps copies) and "
                          "print its read + write GB/s: the rate a plain stream reaches on this GPU")
@@ -288,6 +348,8 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"[bench] copied {n} bytes 3 times")
         return 0
+    if args.mfma_rate:
+        return bench_mfma_rate(args, dev)
     if args.copy_rate:
         n = args.copy_rate << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)

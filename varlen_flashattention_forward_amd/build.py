@@ -19,6 +19,9 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 ROOT = PKG.parent
 LIB = Path(os.environ.get("AVF_LIB_OUT", PKG / "libattn_varlen.so"))
+# the benchmark's roofline calibration kernel, in a library of its own
+PROBE_LIB = PKG / "libavf_probe.so"
+PROBE_SOURCE = "avf_probe.hip"
 BUILD_DIR = Path(os.environ.get("AVF_BUILD_DIR", PKG / "_build"))
 SOURCES = ["avf_api.hip", "avf_kernel.hip", "avf_bwd_kernel.hip", "avf_bwd_dkdv_small.hip", "avf_planner.hip",
            "avf_quant.hip"]
@@ -73,7 +76,23 @@ def build(verbose: bool = False) -> Path:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = False) -> Path:
+    """libavf_probe.so: the MFMA-rate calibration kernel bench.py --mfma-rate runs."""
+    BUILD_DIR.mkdir(parents=True, exist_ok=True)
+    tmp = PROBE_LIB.with_suffix(".so.tmp")
+    cmd = [hipcc(), "-shared", str(CSRC / PROBE_SOURCE), "-o", str(tmp)] + common_flags(PROBE_SOURCE)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("building libavf_probe.so failed")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
