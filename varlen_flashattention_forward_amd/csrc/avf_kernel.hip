@@ -163,7 +163,7 @@ struct Tile {
 // K/V stage per tile, LDS for one stage only, so that two workgroups of NW
 // waves share a CU and one's loads overlap the other's arithmetic.
 template <int D, int QB, int NW, int BN, bool CAUSAL, bool DEVPLAN, bool F8, bool ONE>
-__global__ void __launch_bounds__(NW * 64, 8 / (NW * QB)) avf_fwd_kernel(const AvfLaunchArgs a) {
+__global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunchArgs a) {
     using T = Tile<D, QB, NW, BN, F8, ONE>;
     constexpr int BM = T::BM;
     __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
