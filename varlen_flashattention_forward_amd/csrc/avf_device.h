@@ -51,6 +51,19 @@ __device__ inline void load_lds16(i32x4 rsrc, uint32_t lds_addr, uint32_t voffse
 #endif
 }
 
+// load_lds16 with a wave-uniform byte offset `soffset` (an SGPR) added to the
+// lane's `voffset`, so that loads of one lane that differ by a uniform stride
+// share one offset register and need no per-load vector arithmetic.
+__device__ inline void load_lds16_so(i32x4 rsrc, uint32_t lds_addr, uint32_t voffset, uint32_t soffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voffset), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soffset)),
+                   "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "memory");
+#endif
+}
+
 // Marks `x` as read and rewritten at this point of the instruction stream
 // (emits nothing). Between scheduling fences this keeps a pure arithmetic
 // result where the source computes it instead of letting the optimizer sink

@@ -311,6 +311,25 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
             return;
         }
         const i32x4 krs = rsrc_words(kp, (uint32_t)(nk - 1) * k_rs + 2 * D);
+        // A full stage at D = 64 or 128: load m of a lane fetches key
+        // key0 + m * KSTEP at the same chunk slot, and both swizzles depend on
+        // the key only modulo KSTEP, so one lane offset per array serves every
+        // load and the per-load step goes into the wave-uniform soffset.
+        constexpr int KSTEP = T::NL * 1024 / T::ROWB;
+        constexpr bool AFFINE = 1024 % T::ROWB == 0 && KSTEP % 16 == 0;
+        if (AFFINE && nk == BN) {
+            const int key0 = (wave * 1024 + 16 * lane) / T::ROWB;
+            const int slot = ((16 * lane) % T::ROWB) >> 4;
+            const uint32_t ko = (uint32_t)key0 * k_rs + ((slot ^ k_swz<D>(key0)) << 4);
+            const uint32_t vo = (uint32_t)key0 * v_rs + ((slot ^ v_swz<D>(key0)) << 4);
+#pragma unroll
+            for (int m = 0; m < T::NI / T::NL; ++m) {
+                const int i = wave + T::NL * m;
+                if (do_k) load_lds16_so(krs, kl + i * 1024, ko, (uint32_t)(m * KSTEP) * k_rs);
+                if (do_v) load_lds16_so(vrs, vl + i * 1024, vo, (uint32_t)(m * KSTEP) * v_rs);
+            }
+            return;
+        }
 #pragma unroll
         for (int m = 0; m < T::NI / T::NL; ++m) {
             const int i = wave + T::NL * m;
@@ -775,6 +794,10 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
     const uint32_t o_rs = (uint32_t)(a.o_row * 2);
     char* optr = (char*)a.o + 2 * (avf_elem_offset(q_tok0, a.o_row, h, a.o_head) + gseg * a.o_seg);
     const auto ors = make_rsrc(optr, (uint32_t)(rows_here - 1) * o_rs + 2 * D);
+    // the tile's LSE rows (fp32, contiguous per head): stores are clipped to
+    // them like the O stores
+    float* lptr = a.lse ? a.lse + ((int64_t)h * a.lse_head + q_tok0 + gseg * a.lse_seg) : nullptr;
+    const auto lrs = make_rsrc(lptr, (uint32_t)rows_here * 4);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l_tot = l_i[qb] + __shfl_xor(l_i[qb], 32);
@@ -794,7 +817,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
             if (hf == 0 && a.lse != nullptr) {
                 // natural-log LSE: m*scale + ln l (any reference m gives the same value)
                 const float lse = l_tot > 0.f ? m_i[qb] * lse_scale + __logf(l_tot) : -INFINITY;
-                a.lse[(int64_t)h * a.lse_head + q_tok0 + row + gseg * a.lse_seg] = lse;
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse), lrs, (uint32_t)row * 4, 0, 0);
             }
         }
     }
