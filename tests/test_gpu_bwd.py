@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import blas_oracle
 import varlen_flashattention_forward_amd as avf
 from varlen_flashattention_forward_amd.workloads import WORKLOADS, custom, make_dout, make_inputs, sample_rows
 
@@ -284,6 +285,31 @@ def test_bwd_stride_threshold_pair_full_gradients(split):
     print(f"[bwd threshold split={split}] second segment {stats}", flush=True)
     del t, dout, gbuf, got
     torch.cuda.empty_cache()
+
+
+LONG = {
+    # one long segment, every element of dq, dk and dv compared
+    "self_32768_d128": (128, 4, [0, 32768], [0, 32768], False),
+    "cross_causal_24576x40000_d96": (96, 4, [0, 24576], [0, 40000], True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LONG))
+def test_bwd_long_segment_full_gradients(name):
+    """A segment of tens of thousands of rows (hundreds of dK/dV and dQ tiles
+    along each axis): dq, dk and dv compared element by element against the
+    numpy fp64 backward, which takes the same chain rule as the C oracle with
+    whole-matrix steps so that it finishes in tens of seconds at this size."""
+    D, H, cu_q, cu_k, causal = LONG[name]
+    announce(f"bwd long segment {name}")
+    w = custom(f"bwd_long_{name}", H, D, cu_q, cu_k, std=0.5)
+    t = make_inputs(w, "cuda", seed=71)
+    dout, _ = make_dout(w, "cuda", seed=72)
+    got = backward(t, w, dout, causal)
+    q, k, v = (t[n].contiguous().cpu() for n in ("q", "k", "v"))
+    ref = blas_oracle.attn_varlen_bwd(q, k, v, dout.contiguous().cpu(), w.cu_q, w.cu_k, f32(w.softmax_scale),
+                                      causal=causal)
+    check_all(name, got, ref, w)
 
 
 def test_bwd_many_segments_span_launches():

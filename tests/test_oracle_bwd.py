@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import blas_oracle
 
 ROOT = Path(__file__).resolve().parents[1]
 
@@ -63,6 +64,14 @@ def rand_case(rng, cu_q, cu_k, H, D, std=1.0):
     v = to_bf16_bits(rng.standard_normal((nk, H, D)) * std)
     g = to_bf16_bits(rng.standard_normal((nq, H, D)) * std)
     return q, k, v, g
+
+
+def blas_bwd():
+    """The numpy fp64 backward (oracle/blas_oracle.py), held to the same pins."""
+    def F(q, k, v, g, cu_q, cu_k, scale, causal=False):
+        return blas_oracle.attn_varlen_bwd(q, k, v, g, cu_q, cu_k, scale, causal=causal, row_chunk=7, threads=2)
+    F.library = None
+    return F
 
 
 def c_bwd(library=None):
@@ -220,6 +229,28 @@ def built_oracle():
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
 def test_bwd_oracle_pin(pin, built_oracle):
     pin(c_bwd())
+
+
+@pytest.mark.parametrize("pin", PINS[:-1], ids=lambda p: p.__name__)
+def test_blas_bwd_oracle_pin(pin, built_oracle):
+    """The same pins hold the numpy backward (row chunks of 7 rows, so every
+    case spans several chunks and the chunk boundaries of dK and dV); the
+    row-mode pin is the C library's own."""
+    pin(blas_bwd())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_blas_bwd_agrees_with_c_bwd(causal, built_oracle):
+    """Two independent implementations of the same chain rule agree on ragged
+    segments with empty ones (the C oracle loops per row in fp64; the numpy one
+    uses matrix products in row chunks)."""
+    rng = np.random.default_rng(11)
+    cu_q, cu_k = [0, 61, 61, 140, 141], [0, 45, 80, 80, 203]
+    q, k, v, g = rand_case(rng, cu_q, cu_k, 3, 32)
+    a = c_bwd()(q, k, v, g, cu_q, cu_k, 0.17, causal=causal)
+    b = blas_oracle.attn_varlen_bwd(q, k, v, g, cu_q, cu_k, 0.17, causal=causal, row_chunk=16, threads=3)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(y, x, rtol=0, atol=1e-12)
 
 
 def test_preprocess_reduction():
