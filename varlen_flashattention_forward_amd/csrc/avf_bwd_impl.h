@@ -158,6 +158,27 @@ __device__ inline void store_rows_t(void* base, int64_t row_stride, int32_t nrow
         }
 }
 
+// f(std::integral_constant<int, i>) for i = B .. E-1, in order
+template <int B, int E, typename F>
+__device__ inline void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// dK/dV sub-block slots (KS = D/16 MFMA slots per product, DB = D/32): the
+// scaled exponent of element e (its exp2 and, for a pair, the bf16 packing
+// follow one slot apart), and the dP - D step of its dS (then the product
+// and the packing). Elements 0-7 feed the first 16-row half of the P and dS
+// operands, 8-15 the second.
+constexpr int dkdv_p_slot(int e, int KS, int DB) {
+    return e < 8 ? KS + 1 + e * (KS - 3) / 8 : 2 * KS - 2 + (e - 8) * DB / 8;
+}
+constexpr int dkdv_ds_slot(int e, int KS, int DB) {
+    return e < 8 ? 2 * KS + 1 + e * (KS - 3) / 8 : 3 * KS - 2 + (e - 8) * DB / 8;
+}
+
 // ---------------------------------------------------------------------------
 // dK/dV: one workgroup per (segment, head, block of 32*NW keys); wave w owns
 // keys [w*32, +32) of the block with their K and V rows in registers and
@@ -239,62 +260,119 @@ __global__ void __launch_bounds__(NW * 64, MINB) avf_bwd_dkdv_kernel(const AvfBw
     // MASKED (compile-time): rows past the segment end, and with the causal
     // mask keys past the row's limit, get P = dS = 0 (selected, so garbage
     // LSE/D of padding rows never enters).
+    // A sub-block is written slot by slot, one MFMA per slot, with a
+    // scheduling fence between slots: S (KS slots), dP (KS), dV from the
+    // weights of rows 0-15 and 16-31 of the 32x32 result (DB each), then dK
+    // the same way. Each slot reads the A operand of the MFMA two slots on,
+    // and carries a share of the VALU work, placed after the MFMA whose
+    // result it needs has had a slot to finish and before the first MFMA
+    // that takes it: the weights P of the lane's rows 0-7 (elements 0-7)
+    // during dP and of rows 8-15 early in dV, dS likewise one group later.
+    // The per-accumulator MFMA order is unchanged (t = 0 before t = 1).
     auto stage = [&](int32_t j, int buf, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
+        constexpr int NSL = 4 * KS;
         const char* sbase = lds + buf * STAGE;
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) {
             const char* qrows = sbase + sb * 32 * ROWB;
             const char* grows = sbase + OFF_DO + sb * 32 * ROWB;
-            f32x16 s = {}, dp = {};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qrows + fo.row[ks]);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
-            }
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 ga = *reinterpret_cast<const bf16x8*>(grows + fo.row[ks]);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
-            }
-            // this lane's 16 rows: sb*32 + 8*g + 4*hf + (0..3), g = 0..3
+            // A operand of MFMA slot m: Q rows, dO rows, then dO^T and Q^T
+            // (transposed reads) for t = 0, 1
+            auto read_a = [&](auto mc) -> bf16x8 {
+                constexpr int m = decltype(mc)::value;
+                if constexpr (m < KS) {
+                    return *reinterpret_cast<const bf16x8*>(qrows + fo.row[m]);
+                } else if constexpr (m < 2 * KS) {
+                    return *reinterpret_cast<const bf16x8*>(grows + fo.row[m - KS]);
+                } else {
+                    constexpr int grp = (m - 2 * KS) / DB, d = (m - 2 * KS) % DB;
+                    const char* b = (grp < 2 ? grows : qrows) + (grp & 1) * 16 * ROWB;
+                    return read_tr8(b + fo.tr[0][d], b + fo.tr[1][d]);
+                }
+            };
+            // element e of the lane: row sb*32 + 8*(e/4) + 4*hf + e%4 of the stage
+            auto row_ok = [&](int e) {
+                const int32_t row = j * BQ + sb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+                bool ok = row < lq;
+                if constexpr (CAUSAL) ok = ok && (wkey0 + l32 <= row + coff);
+                return ok;
+            };
+            f32x16 sacc, dpacc;
             float4 lse4[4], del4[4];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int r = sb * 32 + 8 * g + 4 * hf;
-                lse4[g] = *reinterpret_cast<const float4*>(sbase + OFF_LSE + 4 * r);
-                del4[g] = *reinterpret_cast<const float4*>(sbase + OFF_DEL + 4 * r);
-            }
+            float nl[16], x[16], pw[16], y[16], dsv[16];
             bf16x8 pb[2], db16[2];
+            bf16x8 abuf[3];
+            static_for<-2, NSL>([&](auto tc) {
+                constexpr int t = decltype(tc)::value;
+                if constexpr (t + 2 < NSL) abuf[(t + 2) % 3] = read_a(std::integral_constant<int, t + 2>{});
+                if constexpr (t == -2) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int g = e >> 2, i = e & 3;
-                const float lse = i == 0 ? lse4[g].x : i == 1 ? lse4[g].y : i == 2 ? lse4[g].z : lse4[g].w;
-                const float del = i == 0 ? del4[g].x : i == 1 ? del4[g].y : i == 2 ? del4[g].z : del4[g].w;
-                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lse * kLog2e));
-                float ds = p * (dp[e] - del);
-                if constexpr (MASKED) {
-                    const int32_t row = j * BQ + sb * 32 + 8 * g + 4 * hf + i;
-                    bool ok = row < lq;
-                    if constexpr (CAUSAL) ok = ok && (wkey0 + l32 <= row + coff);
-                    p = ok ? p : 0.f;
-                    ds = ok ? ds : 0.f;
+                    for (int g = 0; g < 4; ++g)
+                        lse4[g] = *reinterpret_cast<const float4*>(sbase + OFF_LSE + 4 * (sb * 32 + 8 * g + 4 * hf));
                 }
-                pb[e >> 3][e & 7] = (__bf16)p;
-                db16[e >> 3][e & 7] = (__bf16)ds;
-            }
+                if constexpr (t == 2 * KS - 3) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const char* gt = grows + t * 16 * ROWB;
-                const char* qt = qrows + t * 16 * ROWB;
-#pragma unroll
-                for (int d = 0; d < DB; ++d) {
-                    const bf16x8 ga = read_tr8(gt + fo.tr[0][d], gt + fo.tr[1][d]);
-                    dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pb[t], dv[d], 0, 0, 0);
-                    const bf16x8 qa = read_tr8(qt + fo.tr[0][d], qt + fo.tr[1][d]);
-                    dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, db16[t], dk[d], 0, 0, 0);
+                    for (int g = 0; g < 4; ++g)
+                        del4[g] = *reinterpret_cast<const float4*>(sbase + OFF_DEL + 4 * (sb * 32 + 8 * g + 4 * hf));
                 }
-            }
+                if constexpr (t >= 0) {
+                    const bf16x8 A = abuf[t % 3];
+                    const f32x16 zero = {};
+                    if constexpr (t < KS) {
+                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, kf[t], t == 0 ? zero : sacc, 0, 0, 0);
+                    } else if constexpr (t < 2 * KS) {
+                        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, vf[t - KS], t == KS ? zero : dpacc, 0, 0, 0);
+                    } else {
+                        constexpr int grp = (t - 2 * KS) / DB, d = (t - 2 * KS) % DB;
+                        if constexpr (grp < 2)
+                            dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, pb[grp], dv[d], 0, 0, 0);
+                        else
+                            dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, db16[grp - 2], dk[d], 0, 0, 0);
+                    }
+                }
+                static_for<0, 16>([&](auto ec) {
+                    constexpr int e = decltype(ec)::value;
+                    constexpr int pf = dkdv_p_slot(e, KS, DB), dsub = dkdv_ds_slot(e, KS, DB);
+                    if constexpr (t == (e < 8 ? KS - 2 : KS - 1)) {
+                        const float4 v = lse4[e >> 2];
+                        nl[e] = -((e & 3) == 0 ? v.x : (e & 3) == 1 ? v.y : (e & 3) == 2 ? v.z : v.w) * kLog2e;
+                        pin(nl[e]);
+                    }
+                    if constexpr (t == pf) {
+                        x[e] = __builtin_fmaf(sacc[e], c, nl[e]);
+                        pin(x[e]);
+                    } else if constexpr (t == pf + 1) {
+                        pw[e] = __builtin_amdgcn_exp2f(x[e]);
+                        pin(pw[e]);
+                    } else if constexpr (t == pf + 2 && (e & 1)) {
+                        float p0 = pw[e - 1], p1 = pw[e];
+                        if constexpr (MASKED) {
+                            p0 = row_ok(e - 1) ? p0 : 0.f;
+                            p1 = row_ok(e) ? p1 : 0.f;
+                        }
+                        bf16x2 w = {(__bf16)p0, (__bf16)p1};
+                        pin(w);
+                        pb[e >> 3][(e & 7) - 1] = w[0];
+                        pb[e >> 3][e & 7] = w[1];
+                    }
+                    if constexpr (t == dsub) {
+                        const float4 v = del4[e >> 2];
+                        y[e] = dpacc[e] - ((e & 3) == 0 ? v.x : (e & 3) == 1 ? v.y : (e & 3) == 2 ? v.z : v.w);
+                        pin(y[e]);
+                    } else if constexpr (t == dsub + 1) {
+                        dsv[e] = pw[e] * y[e];
+                        if constexpr (MASKED) dsv[e] = row_ok(e) ? dsv[e] : 0.f;
+                        pin(dsv[e]);
+                    } else if constexpr (t == dsub + 2 && (e & 1)) {
+                        bf16x2 w = {(__bf16)dsv[e - 1], (__bf16)dsv[e]};
+                        pin(w);
+                        db16[e >> 3][(e & 7) - 1] = w[0];
+                        db16[e >> 3][e & 7] = w[1];
+                    }
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
         }
     };
 
