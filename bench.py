@@ -296,6 +296,61 @@ def bench_mfma_rate(args, dev) -> int:
     return 0
 
 
+COISSUE_VARIANTS = [(0, 0), (4, 0), (8, 0), (16, 0), (0, 1), (0, 2), (0, 4), (3, 1), (4, 2)]
+
+
+def bench_coissue(args, dev) -> int:
+    """What VALU instructions next to the MFMAs cost the MFMA pipe (the
+    co-issue kernel of libavf_probe.so): slots of one bf16 MFMA plus nfma
+    v_fma_f32 and nexp v_exp_f32, at one and two waves per SIMD. Reports the
+    time per MFMA slot per SIMD and its ratio to the MFMA-only slot."""
+    import ctypes
+
+    import torch
+
+    from varlen_flashattention_forward_amd import build as avf_build
+
+    if not avf_build.PROBE_LIB.exists():
+        raise RuntimeError(f"{avf_build.PROBE_LIB} is missing: build with python -m varlen_flashattention_forward_amd.build")
+    P = ctypes.CDLL(str(avf_build.PROBE_LIB))
+    P.avf_probe_coissue.restype = ctypes.c_int32
+    P.avf_probe_coissue.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 20000
+    out = torch.empty(2 * cus * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+    for wps in (1, 2):
+        wgs = wps * cus  # 4 waves per workgroup: wps waves per SIMD
+        base = None
+        for nfma, nexp in COISSUE_VARIANTS:
+            def launch():
+                rc = P.avf_probe_coissue(nfma, nexp, out.data_ptr(), wgs, iters, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"avf_probe_coissue returned {rc}")
+            for _ in range(max(1, args.warmup)):
+                launch()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            ns_slot = ms * 1e6 / (wps * iters * 8)
+            base = ns_slot if base is None else base
+            rows.append({"waves_per_simd": wps, "fma_per_slot": nfma, "exp_per_slot": nexp, "ms": round(ms, 4),
+                         "ns_per_slot_per_simd": round(ns_slot, 3), "vs_mfma_only": round(ns_slot / base, 3)})
+            log(f"[coissue] waves/SIMD {wps} fma {nfma:2d} exp {nexp}: {ns_slot:.3f} ns per MFMA slot per SIMD "
+                f"({ns_slot / base:.3f} x MFMA only)")
+    print(json.dumps({"metric": "MFMA slot time with VALU co-issue", "unit": "ns per MFMA slot per SIMD",
+                      "compute_units": cus, "iters": iters, "slots_per_iter": 8, "steps": args.steps,
+                      "results": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -316,6 +371,8 @@ def main() -> int:
                     help="only run a plain device-to-device copy of MIB MiB three times (scales HBM counters)")
     ap.add_argument("--head-major", action="store_true",
                     help="the workload's q, k, v and out as head-major views (row stride D, head stride tokens*D)")
+    ap.add_argument("--coissue", action="store_true",
+                    help="time MFMA slots with v_fma_f32 / v_exp_f32 co-issued (probe library)")
     ap.add_argument("--mfma-rate", choices=["random", "ones"], default=None,
                     help="only time the roofline calibration kernel: a plain stream of bf16 MFMAs "
                          "(v_mfma_f32_32x32x16_bf16) on N(0,1) random or all-ones bf16 operands, two waves per SIMD")
@@ -350,6 +407,8 @@ def main() -> int:
         return 0
     if args.mfma_rate:
         return bench_mfma_rate(args, dev)
+    if args.coissue:
+        return bench_coissue(args, dev)
     if args.copy_rate:
         n = args.copy_rate << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)

@@ -553,3 +553,26 @@ def test_bench_kernel_hash_ignores_comments(tmp_path, monkeypatch):
     assert bench.kernel_hash() == h0
     src.write_text(src.read_text() + "\nstatic int avf_extra_code;\n")
     assert bench.kernel_hash() != h0
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """The calibration library (bench.py --mfma-rate / --coissue) loads and
+    rejects bad arguments before any HIP call."""
+    import ctypes
+
+    from varlen_flashattention_forward_amd import build as avf_build
+
+    if not avf_build.PROBE_LIB.exists():
+        pytest.skip("probe library not built")
+    P = ctypes.CDLL(str(avf_build.PROBE_LIB))
+    P.avf_probe_coissue.restype = ctypes.c_int32
+    P.avf_probe_coissue.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_void_p]
+    P.avf_probe_mfma.restype = ctypes.c_int32
+    P.avf_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    fake = ctypes.c_void_p(4096)
+    assert P.avf_probe_coissue(5, 0, fake, 1, 1, None) == -2    # not an instantiated variant
+    assert P.avf_probe_coissue(4, 0, None, 1, 1, None) == -2    # no output buffer
+    assert P.avf_probe_coissue(4, 0, fake, 0, 1, None) == -2    # no workgroups
+    assert P.avf_probe_mfma(fake, fake, 1, 3, None) == -2       # odd iteration count
+    assert P.avf_probe_mfma(ctypes.c_void_p(4097), fake, 1, 2, None) == -2  # misaligned operands
