@@ -559,8 +559,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
                         pw[qb][e] = __builtin_amdgcn_exp2f(x[qb][e]);
                         pin(pw[qb][e]);
                     } else if (t == te + 2) {
-                        acc[qb][e & 1] = e < 2 ? pw[qb][e] : acc[qb][e & 1] + pw[qb][e];
-                        pin(acc[qb][e & 1]);
+                        // elements 0 and 1 open the two partial sums with
+                        // elements 2 and 3 (no copy into the accumulator)
+                        if (e >= 2) {
+                            acc[qb][e & 1] = (e < 4 ? pw[qb][e - 2] : acc[qb][e & 1]) + pw[qb][e];
+                            pin(acc[qb][e & 1]);
+                        }
                         if (e & 1) {
                             bf16x2 w = {(__bf16)pw[qb][e - 1], (__bf16)pw[qb][e]};
                             pin(w);
@@ -615,8 +619,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
                         pw[qb][e] = __builtin_amdgcn_exp2f(x[qb][e]);
                         pin(pw[qb][e]);
                     } else if (t == te + 2) {
-                        acc[qb][e & 1] = e < 2 ? pw[qb][e] : acc[qb][e & 1] + pw[qb][e];
-                        pin(acc[qb][e & 1]);
+                        // elements 0 and 1 open the two partial sums with
+                        // elements 2 and 3 (no copy into the accumulator)
+                        if (e >= 2) {
+                            acc[qb][e & 1] = (e < 4 ? pw[qb][e - 2] : acc[qb][e & 1]) + pw[qb][e];
+                            pin(acc[qb][e & 1]);
+                        }
                         if (e & 1) {
                             bf16x2 w = {(__bf16)pw[qb][e - 1], (__bf16)pw[qb][e]};
                             pin(w);
