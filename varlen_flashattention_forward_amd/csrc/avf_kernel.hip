@@ -347,9 +347,11 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
     // and V^T rows (32 dims x 16 keys per MFMA).
     // K: lane reads chunk (2*ks + hf) of key sub*32 + l32 (16 bytes). The
     // swizzle depends on the key only modulo 32, so within a buffer the
-    // per-lane byte offsets are fixed; kcur holds them for the K buffer being
-    // read now and moves to the other buffer once per stage, so every
-    // fragment read is one LDS instruction with an immediate sub-block offset.
+    // per-lane byte offsets are fixed; kcur holds them for K buffer 0, and a
+    // read adds the buffer's and the sub-block's offsets. In the stages of
+    // the hot loop the buffer is known at compile time (the loop runs them in
+    // pairs), so every fragment read there is one LDS instruction with an
+    // immediate offset.
     constexpr int SUB = 32 * T::ROWB;    // bytes per 32-key sub-block of V (and of bf16 K)
     constexpr int SUBK = 32 * T::KROWB;  // ... of K
     // F8: depth-64 fragment t of the lane is chunks 4t + 2*hf and 4t + 2*hf + 1
@@ -496,14 +498,14 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
     bf16x8 fr[F8 ? 1 : T::KS];      // rotating K / V^T fragment registers
     i32x8 kf8[F8 ? T::KQ : 1];      // F8: K fragments (refilled one iteration ahead)
     bf16x8 vfr[F8 ? T::KS : 1];     // F8: V^T fragments (refilled one iteration ahead)
-    // K fragment u of sub-block `sub` of the K buffer being read
-    auto read_k = [&](int sub, int u) {
-        return *reinterpret_cast<const bf16x8*>(lds + kcur[u] + sub * SUB);
+    // K fragment u of sub-block `sub` of the K buffer at byte offset kbo
+    auto read_k = [&](int kbo, int sub, int u) {
+        return *reinterpret_cast<const bf16x8*>(lds + kcur[u] + kbo + sub * SUB);
     };
     // F8: depth-64 K fragment t of sub-block `sub`
-    auto read_k8 = [&](int sub, int t) {
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(lds + kcur[2 * t] + sub * SUBK);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(lds + kcur[2 * t + 1] + sub * SUBK);
+    auto read_k8 = [&](int kbo, int sub, int t) {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(lds + kcur[2 * t] + kbo + sub * SUBK);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(lds + kcur[2 * t + 1] + kbo + sub * SUBK);
         return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
     auto mfma8 = [](const i32x8& ka, const i32x8& qa, const f32x16& acc) {
@@ -518,7 +520,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
     // vsub: V sub-block g-1; ksub: K sub-block g+2 (refill_k false when there
     // is none), each in the buffer its address set points at
     auto iterate = [&](const f32x16 (&sv)[QB], f32x16 (&snext)[QB], bool do_qk, const bf16x8 (&pprev)[QB][2],
-                       bf16x8 (&pcur)[QB][2], float (&psum)[QB], int vsub, int ksub, bool refill_k) {
+                       bf16x8 (&pcur)[QB][2], float (&psum)[QB], int vsub, int kbo, int ksub, bool refill_k) {
         constexpr int NSLOT = 2 * T::KS;
         // Softmax element e (of the lane's 16 scores) belongs to slot
         // e * (NSLOT - 2) / 16; its three dependent steps run one slot apart:
@@ -545,7 +547,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[u], pprev[qb][k2], o[qb][db], 0, 0, 0);
-                if (refill_k) fr[u] = read_k(ksub, u);
+                if (refill_k) fr[u] = read_k(kbo, ksub, u);
             }
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -586,7 +588,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
     // multiplies); the softmax of sub-block g spreads over all KQ + KS slots
     // as in `iterate`. vsub: sub-block g in the current V buffer.
     auto iterate8 = [&](const f32x16 (&sv)[QB], f32x16 (&snext)[QB], bool do_qk, const bf16x8 (&pprev)[QB][2],
-                        bf16x8 (&pcur)[QB][2], float (&psum)[QB], int vsub, int ksub, bool refill_k) {
+                        bf16x8 (&pcur)[QB][2], float (&psum)[QB], int vsub, int kbo, int ksub, bool refill_k) {
         constexpr int NSLOT = T::KQ + T::KS;
         float x[QB][16], pw[QB][16], acc[QB][2];
 #pragma unroll
@@ -599,7 +601,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
                         snext[qb] = mfma8(kf8[t], qf8[qb][t], t == 0 ? zero : snext[qb]);
                     }
                 }
-                if (refill_k) kf8[t] = read_k8(ksub, t);
+                if (refill_k) kf8[t] = read_k8(kbo, ksub, t);
             } else if (t < NSLOT) {
                 const int u = t - T::KQ, k2 = u / T::DB, db = u % T::DB;
 #pragma unroll
@@ -641,14 +643,16 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
     };
 
     // `last` (compile-time) marks the segment's final stage: keys past the
-    // segment end are masked and there is no next stage. vnext is the V
-    // buffer stage j+2 is loaded into. At the barrier the K reads move on to
-    // stage j+1's buffer (kcur += kdelta); at sub-block 1 the V reads move
+    // segment end are masked and there is no next stage. kp is stage j's K
+    // buffer, a compile-time constant in the hot loop; vnext is the V buffer
+    // stage j+2 is loaded into. K reads of sub-blocks of stage j+1 (from the
+    // barrier on) use the other K buffer; at sub-block 1 the V reads move
     // from stage j-1's buffer to stage j's (vcur += vdelta).
     // `masked` (compile-time) applies the per-row key limit: the last stage
     // (segment or tile end) and, with the causal mask, the stages that cross
     // the tile's diagonal.
-    auto stage = [&](int32_t j, int kbuf, int vnext, int kdelta, int vdelta, auto last, auto masked) {
+    auto stage = [&](int32_t j, auto kp, int vnext, int vdelta, auto last, auto masked) {
+        const int kbuf = kp;
         constexpr bool LAST = decltype(last)::value;
         constexpr bool MASKED = decltype(masked)::value || LAST;
         int32_t lim[QB];
@@ -675,8 +679,6 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
                     } else {
                         if (j + 2 < nkt) load_stage(j + 2, kbuf, vnext);
                     }
-#pragma unroll
-                    for (int u = 0; u < NKC; ++u) kcur[u] += kdelta;
                 }
             }
             // V reads move to stage j's buffer where they first read it: at
@@ -700,12 +702,14 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
             if (MASKED) mask(kb, lim, sc[kb & 1]);
             float psum[QB];
             // sub-block g-1 has the other parity
+            // K sub-block g+2 lies in this stage's buffer or in the next one's
+            const int kbo = (T::KBUF == 1 || kb + 2 < T::KB ? kbuf : kbuf ^ 1) * T::KSBYTES;
             if constexpr (F8)
                 iterate8(sc[kb & 1], sc[(kb + 1) & 1], !(LAST && kb == T::KB - 1), pk[(kb + 1) & 1], pk[kb & 1], psum,
-                         kb, (kb + 2) % T::KB, kb + 2 < T::KB || !LAST);
+                         kb, kbo, (kb + 2) % T::KB, kb + 2 < T::KB || !LAST);
             else
                 iterate(sc[kb & 1], sc[(kb + 1) & 1], !(LAST && kb == T::KB - 1), pk[(kb + 1) & 1], pk[kb & 1], psum,
-                        kb > 0 ? kb - 1 : T::KB - 1, (kb + 2) % T::KB, kb + 2 < T::KB || !LAST);
+                        kb > 0 ? kb - 1 : T::KB - 1, kbo, (kb + 2) % T::KB, kb + 2 < T::KB || !LAST);
             if (over_limit(psum)) fix_reference(sc[kb & 1], pk[kb & 1], psum);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) l_i[qb] += psum[qb];
@@ -744,7 +748,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
         // S(0), then the K fragments of sub-block 1 for the first iteration
         if constexpr (F8) {
 #pragma unroll
-            for (int t = 0; t < T::KQ; ++t) kf8[t] = read_k8(0, t);
+            for (int t = 0; t < T::KQ; ++t) kf8[t] = read_k8(0, 0, t);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const f32x16 zero = {};
@@ -752,16 +756,16 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
                 for (int t = 0; t < T::KQ; ++t) sc[0][qb] = mfma8(kf8[t], qf8[qb][t], t == 0 ? zero : sc[0][qb]);
             }
 #pragma unroll
-            for (int t = 0; t < T::KQ; ++t) kf8[t] = read_k8(1, t);
+            for (int t = 0; t < T::KQ; ++t) kf8[t] = read_k8(0, 1, t);
             // finite V rows for the zero-weight P.V of sub-block -1
 #pragma unroll
             for (int u = 0; u < T::KS; ++u) vfr[u] = read_v(0, u);
         } else {
 #pragma unroll
-            for (int u = 0; u < T::KS; ++u) fr[u] = read_k(0, u);
+            for (int u = 0; u < T::KS; ++u) fr[u] = read_k(0, 0, u);
             qk(fr, sc[0]);
 #pragma unroll
-            for (int u = 0; u < T::KS; ++u) fr[u] = read_k(1, u);
+            for (int u = 0; u < T::KS; ++u) fr[u] = read_k(0, 1, u);
         }
         // Sub-block 0 has no predecessor: its P.V slots multiply zero
         // weights with loaded (finite) V rows instead, which keeps one
@@ -781,22 +785,31 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
             vprev = vnext = vbuf;
             vbuf = vbuf == 2 ? 0 : vbuf + 1;
         };
-        // stages every row sees whole, then the ones crossing the causal diagonal
+        // stages every row sees whole (in pairs, so that each one's K buffer
+        // is a compile-time constant), then the ones crossing the causal
+        // diagonal, then the last
         const int32_t nfree = ONE ? 0 : min(jmask, nkt - 1);
         int32_t j = 0;
-        for (; j < nfree; ++j) {
-            stage(j, kbuf, vnext, kbuf ? -T::KSBYTES : T::KSBYTES, (vbuf - vprev) * T::SBYTES, std::false_type{},
-                  std::false_type{});
+        using K0 = std::integral_constant<int, 0>;
+        using K1 = std::integral_constant<int, 1>;
+        for (; j + 1 < nfree; j += 2) {
+            stage(j, K0{}, vnext, (vbuf - vprev) * T::SBYTES, std::false_type{}, std::false_type{});
             advance();
+            stage(j + 1, K1{}, vnext, (vbuf - vprev) * T::SBYTES, std::false_type{}, std::false_type{});
+            advance();
+        }
+        if (j < nfree) {
+            stage(j, K0{}, vnext, (vbuf - vprev) * T::SBYTES, std::false_type{}, std::false_type{});
+            advance();
+            ++j;
         }
         if constexpr (CAUSAL && !ONE) {
             for (; j + 1 < nkt; ++j) {
-                stage(j, kbuf, vnext, kbuf ? -T::KSBYTES : T::KSBYTES, (vbuf - vprev) * T::SBYTES, std::false_type{},
-                      std::true_type{});
+                stage(j, kbuf, vnext, (vbuf - vprev) * T::SBYTES, std::false_type{}, std::true_type{});
                 advance();
             }
         }
-        stage(nkt - 1, kbuf, vnext, 0, (vbuf - vprev) * T::SBYTES, std::true_type{}, std::true_type{});
+        stage(nkt - 1, kbuf, vnext, (vbuf - vprev) * T::SBYTES, std::true_type{}, std::true_type{});
     }
 
     // ---- epilogue: O = O_acc / l (bf16), LSE = ln sum exp(scale * s) ----
