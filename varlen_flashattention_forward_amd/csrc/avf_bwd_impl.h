@@ -193,9 +193,13 @@ __global__ void __launch_bounds__(NW * 64, MINB) avf_bwd_dkdv_kernel(const AvfBw
     constexpr int SB = BQ / 32;
     constexpr int RBYTES = BQ * ROWB;                  // Q (or dO) rows of a stage
     constexpr int OFF_DO = RBYTES;
+    // LSE rows arrive at OFF_RAW; before the stage's barrier wave 0 stores
+    // them at OFF_LSE as -LSE * log2(e), the offset the weights' exponent
+    // takes, so no wave multiplies them per element
     constexpr int OFF_LSE = 2 * RBYTES;
     constexpr int OFF_DEL = 2 * RBYTES + 4 * BQ;
-    constexpr int STAGE = 2 * RBYTES + 8 * BQ;
+    constexpr int OFF_RAW = 2 * RBYTES + 8 * BQ;
+    constexpr int STAGE = 2 * RBYTES + 12 * BQ;
     static_assert(STAGE % 16 == 0 && BQ % 32 == 0 && BQ <= 64, "stage layout");
     __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
     const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
@@ -250,7 +254,7 @@ __global__ void __launch_bounds__(NW * 64, MINB) avf_bwd_dkdv_kernel(const AvfBw
         if (wave == 0 && lane < BQ / 4) {
             const i32x4 lr = rsrc_words(a.lse + h * a.lse_head + tok, (uint32_t)nrows * 4);
             const i32x4 dr = rsrc_words(a.delta + h * a.delta_head + tok, (uint32_t)nrows * 4);
-            load_lds16(lr, dst + OFF_LSE, 16 * lane);
+            load_lds16(lr, dst + OFF_RAW, 16 * lane);
             load_lds16(dr, dst + OFF_DEL, 16 * lane);
         }
     };
@@ -300,7 +304,7 @@ __global__ void __launch_bounds__(NW * 64, MINB) avf_bwd_dkdv_kernel(const AvfBw
             };
             f32x16 sacc, dpacc;
             float4 lse4[4], del4[4];
-            float nl[16], x[16], pw[16], y[16], dsv[16];
+            float x[16], pw[16], y[16], dsv[16];
             bf16x8 pb[2], db16[2];
             bf16x8 abuf[3];
             static_for<-2, NSL>([&](auto tc) {
@@ -334,13 +338,10 @@ __global__ void __launch_bounds__(NW * 64, MINB) avf_bwd_dkdv_kernel(const AvfBw
                 static_for<0, 16>([&](auto ec) {
                     constexpr int e = decltype(ec)::value;
                     constexpr int pf = dkdv_p_slot(e, KS, DB), dsub = dkdv_ds_slot(e, KS, DB);
-                    if constexpr (t == (e < 8 ? KS - 2 : KS - 1)) {
-                        const float4 v = lse4[e >> 2];
-                        nl[e] = -((e & 3) == 0 ? v.x : (e & 3) == 1 ? v.y : (e & 3) == 2 ? v.z : v.w) * kLog2e;
-                        pin(nl[e]);
-                    }
                     if constexpr (t == pf) {
-                        x[e] = __builtin_fmaf(sacc[e], c, nl[e]);
+                        const float4 v = lse4[e >> 2];  // -LSE * log2(e) of the element's row
+                        x[e] = __builtin_fmaf(sacc[e], c,
+                                              (e & 3) == 0 ? v.x : (e & 3) == 1 ? v.y : (e & 3) == 2 ? v.z : v.w);
                         pin(x[e]);
                     } else if constexpr (t == pf + 1) {
                         pw[e] = __builtin_amdgcn_exp2f(x[e]);
@@ -381,6 +382,12 @@ __global__ void __launch_bounds__(NW * 64, MINB) avf_bwd_dkdv_kernel(const AvfBw
         int buf = 0;
         auto next = [&](int32_t j) {
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            if (wave == 0 && lane < BQ / 4) {
+                char* sb = lds + buf * STAGE;
+                const float4 r = *reinterpret_cast<const float4*>(sb + OFF_RAW + 16 * lane);
+                *reinterpret_cast<float4*>(sb + OFF_LSE + 16 * lane) =
+                    float4{-r.x * kLog2e, -r.y * kLog2e, -r.z * kLog2e, -r.w * kLog2e};
+            }
             __syncthreads();
             if (j + 1 < nst) load_stage(j + 1, buf ^ 1);
         };
