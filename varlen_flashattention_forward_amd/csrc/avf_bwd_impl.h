@@ -169,9 +169,9 @@ __device__ inline void static_for(F&& f) {
 
 // dK/dV sub-block slots (KS = D/16 MFMA slots per product, DB = D/32): the
 // scaled exponent of element e (its exp2 and, for a pair, the bf16 packing
-// follow one slot apart), and the dP - D step of its dS (then the product
-// and the packing). Elements 0-7 feed the first 16-row half of the P and dS
-// operands, 8-15 the second.
+// follow one slot apart), and the product dS = P (dP - D) (the packing
+// follows one slot later). Elements 0-7 feed the first 16-row half of the P
+// and dS operands, 8-15 the second.
 constexpr int dkdv_p_slot(int e, int KS, int DB) {
     return e < 8 ? KS + 1 + e * (KS - 3) / 8 : 2 * KS - 2 + (e - 8) * DB / 8;
 }
@@ -193,13 +193,16 @@ __global__ void __launch_bounds__(NW * 64, MINB) avf_bwd_dkdv_kernel(const AvfBw
     constexpr int SB = BQ / 32;
     constexpr int RBYTES = BQ * ROWB;                  // Q (or dO) rows of a stage
     constexpr int OFF_DO = RBYTES;
-    // LSE rows arrive at OFF_RAW; before the stage's barrier wave 0 stores
-    // them at OFF_LSE as -LSE * log2(e), the offset the weights' exponent
-    // takes, so no wave multiplies them per element
+    // LSE and D rows arrive at OFF_RAW and OFF_RAWD; before the stage's
+    // barrier wave 0 stores them at OFF_LSE as -LSE * log2(e), the offset the
+    // weights' exponent takes, and at OFF_DEL as -D, the initial value of the
+    // dP accumulator (so the MFMA yields dP - D), so no wave spends a VALU
+    // instruction per element on either
     constexpr int OFF_LSE = 2 * RBYTES;
     constexpr int OFF_DEL = 2 * RBYTES + 4 * BQ;
     constexpr int OFF_RAW = 2 * RBYTES + 8 * BQ;
-    constexpr int STAGE = 2 * RBYTES + 12 * BQ;
+    constexpr int OFF_RAWD = 2 * RBYTES + 12 * BQ;
+    constexpr int STAGE = 2 * RBYTES + 16 * BQ;
     static_assert(STAGE % 16 == 0 && BQ % 32 == 0 && BQ <= 64, "stage layout");
     __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
     const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
@@ -255,7 +258,7 @@ __global__ void __launch_bounds__(NW * 64, MINB) avf_bwd_dkdv_kernel(const AvfBw
             const i32x4 lr = rsrc_words(a.lse + h * a.lse_head + tok, (uint32_t)nrows * 4);
             const i32x4 dr = rsrc_words(a.delta + h * a.delta_head + tok, (uint32_t)nrows * 4);
             load_lds16(lr, dst + OFF_RAW, 16 * lane);
-            load_lds16(dr, dst + OFF_DEL, 16 * lane);
+            load_lds16(dr, dst + OFF_RAWD, 16 * lane);
         }
     };
 
@@ -302,9 +305,9 @@ __global__ void __launch_bounds__(NW * 64, MINB) avf_bwd_dkdv_kernel(const AvfBw
                 if constexpr (CAUSAL) ok = ok && (wkey0 + l32 <= row + coff);
                 return ok;
             };
-            f32x16 sacc, dpacc;
-            float4 lse4[4], del4[4];
-            float x[16], pw[16], y[16], dsv[16];
+            f32x16 sacc, dpacc, dinit;
+            float4 lse4[4];
+            float x[16], pw[16], dsv[16];
             bf16x8 pb[2], db16[2];
             bf16x8 abuf[3];
             static_for<-2, NSL>([&](auto tc) {
@@ -315,10 +318,16 @@ __global__ void __launch_bounds__(NW * 64, MINB) avf_bwd_dkdv_kernel(const AvfBw
                     for (int g = 0; g < 4; ++g)
                         lse4[g] = *reinterpret_cast<const float4*>(sbase + OFF_LSE + 4 * (sb * 32 + 8 * g + 4 * hf));
                 }
-                if constexpr (t == 2 * KS - 3) {
+                // -D of the lane's 16 rows: the dP accumulator's initial value
+                if constexpr (t == KS - 3) {
 #pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        del4[g] = *reinterpret_cast<const float4*>(sbase + OFF_DEL + 4 * (sb * 32 + 8 * g + 4 * hf));
+                    for (int g = 0; g < 4; ++g) {
+                        const float4 v = *reinterpret_cast<const float4*>(sbase + OFF_DEL + 4 * (sb * 32 + 8 * g + 4 * hf));
+                        dinit[4 * g] = v.x;
+                        dinit[4 * g + 1] = v.y;
+                        dinit[4 * g + 2] = v.z;
+                        dinit[4 * g + 3] = v.w;
+                    }
                 }
                 if constexpr (t >= 0) {
                     const bf16x8 A = abuf[t % 3];
@@ -326,7 +335,7 @@ __global__ void __launch_bounds__(NW * 64, MINB) avf_bwd_dkdv_kernel(const AvfBw
                     if constexpr (t < KS) {
                         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, kf[t], t == 0 ? zero : sacc, 0, 0, 0);
                     } else if constexpr (t < 2 * KS) {
-                        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, vf[t - KS], t == KS ? zero : dpacc, 0, 0, 0);
+                        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, vf[t - KS], t == KS ? dinit : dpacc, 0, 0, 0);
                     } else {
                         constexpr int grp = (t - 2 * KS) / DB, d = (t - 2 * KS) % DB;
                         if constexpr (grp < 2)
@@ -358,14 +367,10 @@ __global__ void __launch_bounds__(NW * 64, MINB) avf_bwd_dkdv_kernel(const AvfBw
                         pb[e >> 3][e & 7] = w[1];
                     }
                     if constexpr (t == dsub) {
-                        const float4 v = del4[e >> 2];
-                        y[e] = dpacc[e] - ((e & 3) == 0 ? v.x : (e & 3) == 1 ? v.y : (e & 3) == 2 ? v.z : v.w);
-                        pin(y[e]);
-                    } else if constexpr (t == dsub + 1) {
-                        dsv[e] = pw[e] * y[e];
+                        dsv[e] = pw[e] * dpacc[e];  // dpacc holds dP - D
                         if constexpr (MASKED) dsv[e] = row_ok(e) ? dsv[e] : 0.f;
                         pin(dsv[e]);
-                    } else if constexpr (t == dsub + 2 && (e & 1)) {
+                    } else if constexpr (t == dsub + 1 && (e & 1)) {
                         bf16x2 w = {(__bf16)dsv[e - 1], (__bf16)dsv[e]};
                         pin(w);
                         db16[e >> 3][(e & 7) - 1] = w[0];
@@ -385,8 +390,10 @@ __global__ void __launch_bounds__(NW * 64, MINB) avf_bwd_dkdv_kernel(const AvfBw
             if (wave == 0 && lane < BQ / 4) {
                 char* sb = lds + buf * STAGE;
                 const float4 r = *reinterpret_cast<const float4*>(sb + OFF_RAW + 16 * lane);
+                const float4 d = *reinterpret_cast<const float4*>(sb + OFF_RAWD + 16 * lane);
                 *reinterpret_cast<float4*>(sb + OFF_LSE + 16 * lane) =
                     float4{-r.x * kLog2e, -r.y * kLog2e, -r.z * kLog2e, -r.w * kLog2e};
+                *reinterpret_cast<float4*>(sb + OFF_DEL + 16 * lane) = float4{-d.x, -d.y, -d.z, -d.w};
             }
             __syncthreads();
             if (j + 1 < nst) load_stage(j + 1, buf ^ 1);
@@ -471,6 +478,11 @@ __global__ void __launch_bounds__(NW * 64, 2) avf_bwd_dq_kernel(const AvfBwdArgs
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) dq[db][e] = 0.f;
+    // -D of the lane's row in every slot: the dP accumulator's initial value,
+    // so the MFMA yields dP - D
+    f32x16 negd;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) negd[e] = -del;
 
     const FragOffsets<D> fo(lane);
     const float c = a.scale_log2e;
@@ -502,7 +514,7 @@ __global__ void __launch_bounds__(NW * 64, 2) avf_bwd_dq_kernel(const AvfBwdArgs
         for (int sb = 0; sb < SB; ++sb) {
             const char* krows = sbase + sb * 32 * ROWB;
             const char* vrows = sbase + RBYTES + sb * 32 * ROWB;
-            f32x16 s = {}, dp = {};
+            f32x16 s = {}, dp = negd;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krows + fo.row[ks]);
@@ -517,7 +529,7 @@ __global__ void __launch_bounds__(NW * 64, 2) avf_bwd_dq_kernel(const AvfBwdArgs
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lse2));
-                float ds = p * (dp[e] - del);
+                float ds = p * dp[e];  // dp holds dP - D
                 if constexpr (MASKED) {
                     const int key = sb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
                     ds = key < lim ? ds : 0.f;

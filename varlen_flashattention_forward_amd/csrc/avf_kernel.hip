@@ -482,7 +482,11 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
     // and refills its register with the V^T fragment that slot t + KS
     // consumes; slot KS + u consumes that V^T fragment and refills the
     // register with K fragment u of the next iteration. Every LDS read thus
-    // has KS slots to land.
+    // has KS slots to land. At D = 64 and 96 the general configuration has
+    // registers to spare (SPLIT): K and V^T fragments then have a set each,
+    // slot t refills K fragment t for the next iteration and slot KS + u the
+    // V^T fragment u of sub-block g (multiplied in the next iteration), so
+    // every read has a whole iteration to land.
     // The rare reference move (fix_reference) rescales O after the P.V(g-1)
     // MFMAs, so O then holds all earlier sub-blocks against the old reference.
     //
@@ -497,7 +501,8 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
     bf16x8 pk[2][QB][2];   // their weights as bf16 P^T operands
     bf16x8 fr[F8 ? 1 : T::KS];      // rotating K / V^T fragment registers
     i32x8 kf8[F8 ? T::KQ : 1];      // F8: K fragments (refilled one iteration ahead)
-    bf16x8 vfr[F8 ? T::KS : 1];     // F8: V^T fragments (refilled one iteration ahead)
+    constexpr bool SPLIT = !F8 && !ONE && !T::VLAG && D < 128;
+    bf16x8 vfr[(F8 || SPLIT) ? T::KS : 1];  // F8, SPLIT: V^T fragments (refilled one iteration ahead)
     // K fragment u of sub-block `sub` of the K buffer at byte offset kbo
     auto read_k = [&](int kbo, int sub, int u) {
         return *reinterpret_cast<const bf16x8*>(lds + kcur[u] + kbo + sub * SUB);
@@ -517,8 +522,8 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
         const char* p = lds + vcur[db] + sub * SUB + k2 * 16 * T::ROWB;
         return read_tr8(p, p + 8 * T::ROWB);
     };
-    // vsub: V sub-block g-1; ksub: K sub-block g+2 (refill_k false when there
-    // is none), each in the buffer its address set points at
+    // vsub: V sub-block g-1 (SPLIT: g); ksub: K sub-block g+2 (refill_k false
+    // when there is none), each in the buffer its address set points at
     auto iterate = [&](const f32x16 (&sv)[QB], f32x16 (&snext)[QB], bool do_qk, const bf16x8 (&pprev)[QB][2],
                        bf16x8 (&pcur)[QB][2], float (&psum)[QB], int vsub, int kbo, int ksub, bool refill_k) {
         constexpr int NSLOT = 2 * T::KS;
@@ -541,13 +546,21 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
                                                                             0, 0, 0);
                     }
                 }
-                fr[t] = read_v(vsub, t);
+                if constexpr (SPLIT) {
+                    if (refill_k) fr[t] = read_k(kbo, ksub, t);
+                } else {
+                    fr[t] = read_v(vsub, t);
+                }
             } else if (t < NSLOT) {
                 const int u = t - T::KS, k2 = u / T::DB, db = u % T::DB;
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[u], pprev[qb][k2], o[qb][db], 0, 0, 0);
-                if (refill_k) fr[u] = read_k(kbo, ksub, u);
+                    o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(SPLIT ? vfr[u] : fr[u], pprev[qb][k2],
+                                                                        o[qb][db], 0, 0, 0);
+                if constexpr (SPLIT)
+                    vfr[u] = read_v(vsub, u);
+                else if (refill_k)
+                    fr[u] = read_k(kbo, ksub, u);
             }
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -682,22 +695,11 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
                 }
             }
             // V reads move to stage j's buffer where they first read it: at
-            // sub-block 1 (P.V(g-1) reads V of sub-block g-1), with F8 at
-            // sub-block 0 (fragments of sub-block g are read ahead)
-            if (kb == (F8 ? 0 : 1)) {
+            // sub-block 1 (P.V(g-1) reads V of sub-block g-1), with F8 and
+            // SPLIT at sub-block 0 (fragments of sub-block g are read ahead)
+            if (kb == ((F8 || SPLIT) ? 0 : 1)) {
 #pragma unroll
                 for (int db = 0; db < T::DB; ++db) vcur[db] += vdelta;
-            }
-            // D = 96 has the most softmax work per MFMA. Even with the stage
-            // loads on the older wave of each SIMD pair, the older wave still
-            // wins too many MFMA ties there, so the younger wave gets the
-            // higher priority for sub-block 0 of every stage: strided_9728
-            // +2%. At D = 128 the same costs 1%, so there it stays off.
-            if constexpr (NW == 8 && D == 96 && !F8) {
-                if (wave >= NW / 2 && kb == 0)
-                    __builtin_amdgcn_s_setprio(1);
-                else
-                    __builtin_amdgcn_s_setprio(0);
             }
             if (MASKED) mask(kb, lim, sc[kb & 1]);
             float psum[QB];
@@ -709,14 +711,14 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
                          kb, kbo, (kb + 2) % T::KB, kb + 2 < T::KB || !LAST);
             else
                 iterate(sc[kb & 1], sc[(kb + 1) & 1], !(LAST && kb == T::KB - 1), pk[(kb + 1) & 1], pk[kb & 1], psum,
-                        kb > 0 ? kb - 1 : T::KB - 1, kbo, (kb + 2) % T::KB, kb + 2 < T::KB || !LAST);
+                        SPLIT ? kb : (kb > 0 ? kb - 1 : T::KB - 1), kbo, (kb + 2) % T::KB, kb + 2 < T::KB || !LAST);
             if (over_limit(psum)) fix_reference(sc[kb & 1], pk[kb & 1], psum);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) l_i[qb] += psum[qb];
         }
         if (LAST) {
-            // P.V of the segment's final sub-block (F8: its V^T fragments are in vfr)
-            if constexpr (F8) {
+            // P.V of the segment's final sub-block (F8, SPLIT: its V^T fragments are in vfr)
+            if constexpr (F8 || SPLIT) {
 #pragma unroll
                 for (int u = 0; u < T::KS; ++u)
 #pragma unroll
@@ -766,6 +768,11 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
             qk(fr, sc[0]);
 #pragma unroll
             for (int u = 0; u < T::KS; ++u) fr[u] = read_k(0, 1, u);
+            // SPLIT: finite V rows for the zero-weight P.V of sub-block -1
+            if constexpr (SPLIT) {
+#pragma unroll
+                for (int u = 0; u < T::KS; ++u) vfr[u] = read_v(0, u);
+            }
         }
         // Sub-block 0 has no predecessor: its P.V slots multiply zero
         // weights with loaded (finite) V rows instead, which keeps one
