@@ -207,6 +207,27 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
     const char* qptr = (const char*)a.q + 2 * (avf_elem_offset(q_tok0, a.q_row, h, a.q_head) + gseg * a.q_seg);
     const auto qrs = make_rsrc(qptr, (uint32_t)(rows_here - 1) * q_rs + 2 * D);
     const int wrow0 = wave * QB * 32;
+    // A lane's Q fragments are 16-byte pieces of one row, so loading them
+    // straight into registers makes every load instruction touch 32 rows a
+    // token stride apart. With 64-key stages (short segments, a few stages
+    // per tile) the tile's Q rows instead arrive by whole-row direct loads
+    // into V buffers 1 and 2, which hold nothing until stage 0's barrier,
+    // and the fragments are read from there (QLDS); rows past the tile read 0.
+    constexpr bool QLDS = T::VLAG && !F8;
+    constexpr int QOFF = T::KBUF * T::KSBYTES + T::SBYTES;
+    static_assert(!QLDS || (QB == 1 && BM * 2 * D <= 2 * T::SBYTES && (BM * 2 * D / 1024) % NW == 0),
+                  "Q rows fit V buffers 1 and 2");
+    auto load_q_lds = [&]() {
+        const i32x4 qw = rsrc_words(qptr, (uint32_t)(rows_here - 1) * q_rs + 2 * D);
+#pragma unroll
+        for (int m = 0; m < BM * 2 * D / 1024 / NW; ++m) {
+            const int i = wave + NW * m;
+            const int pos = i * 1024 + 16 * lane;
+            const int r = pos / (2 * D);
+            const int slot = (pos % (2 * D)) >> 4;
+            load_lds16(qw, lds_addr + QOFF + i * 1024, (uint32_t)r * q_rs + ((slot ^ k_swz<D>(r)) << 4));
+        }
+    };
     bf16x8 qf[QB][F8 ? 1 : T::KS];
     i32x8 qf8[QB][F8 ? T::KQ : 1];  // F8: lane holds dims 64t + 32*hf .. +32 of its row
     if constexpr (F8) {
@@ -222,7 +243,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
                 const i32x4 hi = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(q8rs, off + 16, 0, 0));
                 qf8[qb][t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
-    } else {
+    } else if constexpr (!QLDS) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -739,6 +760,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
     };
 
     if (nkt > 0) {
+        if constexpr (QLDS) load_q_lds();
         load_stage(0, 0, 0);
         if (!ONE && nkt > 1) load_stage(1, 1, 1, true, !T::VLAG);
         // Wait for everything issued so far (Q fragments and the first two
@@ -747,6 +769,14 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
         // otherwise it would hold the loop's MFMAs on in-flight stage loads.
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
+        // QLDS: the wave's Q fragments (row wrow0 + l32, chunk 2ks + hf, with
+        // the K swizzle); read before stage 0's barrier reloads V buffer 1
+        if constexpr (QLDS) {
+#pragma unroll
+            for (int ks = 0; ks < T::KS; ++ks)
+                qf[0][ks] = *reinterpret_cast<const bf16x8*>(lds + QOFF + (wrow0 + l32) * 2 * D +
+                                                             (((2 * ks + hf) ^ k_swz<D>(l32)) << 4));
+        }
         // S(0), then the K fragments of sub-block 1 for the first iteration
         if constexpr (F8) {
 #pragma unroll
@@ -820,6 +850,19 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
     }
 
     // ---- epilogue: O = O_acc / l (bf16), LSE = ln sum exp(scale * s) ----
+    // A lane holds 8-byte pieces of one O row, so storing them directly
+    // makes every store instruction touch 32 rows (a head's D elements of a
+    // token row, rows a full token stride apart). The rows go through LDS
+    // instead: each wave writes its rows into a slot of its own (pitch 2D +
+    // 16 bytes), reads them back as whole 16-byte chunks and stores them so
+    // that consecutive lanes cover consecutive bytes of a row. For short
+    // segments, where a tile is a few stages long, the direct stores took a
+    // fifth of the kernel's time. One barrier first: the slots overlap the
+    // K/V ring, which other waves may still be reading.
+    constexpr int OP = 2 * D + 16;
+    static_assert(NW * QB * 32 * OP <= T::LDS_BYTES, "O staging fits in the ring");
+    __syncthreads();
+    char* ow = lds + wave * (QB * 32 * OP);
     const uint32_t o_rs = (uint32_t)(a.o_row * 2);
     char* optr = (char*)a.o + 2 * (avf_elem_offset(q_tok0, a.o_row, h, a.o_head) + gseg * a.o_seg);
     const auto ors = make_rsrc(optr, (uint32_t)(rows_here - 1) * o_rs + 2 * D);
@@ -832,23 +875,32 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
         const float l_tot = l_i[qb] + __shfl_xor(l_i[qb], 32);
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const int row = wrow0 + qb * 32 + l32;
-        if (row < rows_here) {
 #pragma unroll
-            for (int db = 0; db < T::DB; ++db)
+        for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    bf16x4 ov;
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 ov;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(o[qb][db][4 * g + e] * inv);
-                    const uint32_t off = (uint32_t)row * o_rs + (db * 32 + 8 * g + 4 * hf) * 2;
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, ov), ors, off, 0, 0);
-                }
-            if (hf == 0 && a.lse != nullptr) {
-                // natural-log LSE: m*scale + ln l (any reference m gives the same value)
-                const float lse = l_tot > 0.f ? m_i[qb] * lse_scale + __logf(l_tot) : -INFINITY;
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse), lrs, (uint32_t)row * 4, 0, 0);
+                for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(o[qb][db][4 * g + e] * inv);
+                *reinterpret_cast<bf16x4*>(ow + (qb * 32 + l32) * OP + (db * 32 + 8 * g + 4 * hf) * 2) = ov;
             }
+        if (row < rows_here && hf == 0 && a.lse != nullptr) {
+            // natural-log LSE: m*scale + ln l (any reference m gives the same value)
+            const float lse = l_tot > 0.f ? m_i[qb] * lse_scale + __logf(l_tot) : -INFINITY;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse), lrs, (uint32_t)row * 4, 0, 0);
         }
+    }
+    // chunk f = 64 i + lane of the wave's rows: row f / (D/8), chunk f % (D/8)
+    constexpr int CPR = D / 8;
+    static_assert((QB * 32 * CPR) % 64 == 0, "whole store instructions");
+#pragma unroll
+    for (int i = 0; i < QB * 32 * CPR / 64; ++i) {
+        const int f = 64 * i + lane;
+        const int r = f / CPR, ch = f % CPR;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(ow + r * OP + ch * 16);
+        if (wrow0 + r < rows_here)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), ors,
+                                                   (uint32_t)(wrow0 + r) * o_rs + ch * 16, 0, 0);
     }
     };
 
