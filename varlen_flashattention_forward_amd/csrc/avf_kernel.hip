@@ -855,10 +855,10 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
     // token row, rows a full token stride apart). The rows go through LDS
     // instead: each wave writes its rows into a slot of its own (pitch 2D +
     // 16 bytes), reads them back as whole 16-byte chunks and stores them so
-    // that consecutive lanes cover consecutive bytes of a row. For short
-    // segments, where a tile is a few stages long, the direct stores took a
-    // fifth of the kernel's time. One barrier first: the slots overlap the
-    // K/V ring, which other waves may still be reading.
+    // that consecutive lanes cover consecutive bytes of a row (short
+    // segments, whose tiles are a few stages long: 7-10% faster). One barrier
+    // first: the slots overlap the K/V ring, which other waves may still be
+    // reading.
     constexpr int OP = 2 * D + 16;
     static_assert(NW * QB * 32 * OP <= T::LDS_BYTES, "O staging fits in the ring");
     __syncthreads();
