@@ -829,24 +829,45 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) avf_fwd_kernel(const AvfLaunc
         int32_t j = 0;
         using K0 = std::integral_constant<int, 0>;
         using K1 = std::integral_constant<int, 1>;
-        for (; j + 1 < nfree; j += 2) {
-            stage(j, K0{}, vnext, (vbuf - vprev) * T::SBYTES, std::false_type{}, std::false_type{});
-            advance();
-            stage(j + 1, K1{}, vnext, (vbuf - vprev) * T::SBYTES, std::false_type{}, std::false_type{});
-            advance();
-        }
-        if (j < nfree) {
-            stage(j, K0{}, vnext, (vbuf - vprev) * T::SBYTES, std::false_type{}, std::false_type{});
-            advance();
-            ++j;
-        }
-        if constexpr (CAUSAL && !ONE) {
-            for (; j + 1 < nkt; ++j) {
-                stage(j, kbuf, vnext, (vbuf - vprev) * T::SBYTES, std::false_type{}, std::true_type{});
+        // A wave none of whose rows lie in the segment (the last query block
+        // of a segment can hold a few rows only) skips the arithmetic and
+        // keeps the stages' barriers and its share of the loads, so its SIMD
+        // partner runs alone on the MFMA pipe. Nothing of it is stored.
+        if (wrow0 >= rows_here) {
+            for (; j < nkt; ++j) {
+                if (j + 1 < nkt || T::VLAG) {
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                    __syncthreads();
+                    if (j + 1 < nkt) {
+                        if constexpr (T::VLAG) {
+                            if (j + 2 < nkt) load_stage(j + 2, j & 1, 0, true, false);
+                            load_stage(j + 1, 0, (j + 1) % 3, false, true);
+                        } else {
+                            if (j + 2 < nkt) load_stage(j + 2, j & 1, (j + 2) % 3);
+                        }
+                    }
+                }
+            }
+        } else {
+            for (; j + 1 < nfree; j += 2) {
+                stage(j, K0{}, vnext, (vbuf - vprev) * T::SBYTES, std::false_type{}, std::false_type{});
+                advance();
+                stage(j + 1, K1{}, vnext, (vbuf - vprev) * T::SBYTES, std::false_type{}, std::false_type{});
                 advance();
             }
+            if (j < nfree) {
+                stage(j, K0{}, vnext, (vbuf - vprev) * T::SBYTES, std::false_type{}, std::false_type{});
+                advance();
+                ++j;
+            }
+            if constexpr (CAUSAL && !ONE) {
+                for (; j + 1 < nkt; ++j) {
+                    stage(j, kbuf, vnext, (vbuf - vprev) * T::SBYTES, std::false_type{}, std::true_type{});
+                    advance();
+                }
+            }
+            stage(nkt - 1, kbuf, vnext, (vbuf - vprev) * T::SBYTES, std::true_type{}, std::true_type{});
         }
-        stage(nkt - 1, kbuf, vnext, (vbuf - vprev) * T::SBYTES, std::true_type{}, std::true_type{});
     }
 
     // ---- epilogue: O = O_acc / l (bf16), LSE = ln sum exp(scale * s) ----
