@@ -18,7 +18,8 @@
 //
 // Matrix layout on the MFMA (v_mfma_f32_32x32x16_bf16, wave64):
 //   S^T = K * Q^T:  A = 32 keys x 16 dims of K (from LDS, one 16-byte read per
-//                   lane), B = Q^T (kept in registers for the whole tile).
+//                   lane), B = Q^T (kept in registers for the whole tile; with
+//                   64-key stages it arrives through LDS by whole-row loads).
 //                   The 32x32 result puts ONE query row per lane pair
 //                   (lane l and l+32, 16 keys each), so the row max needs one
 //                   cross-half exchange and the row sum none until the end.
@@ -28,7 +29,8 @@
 //                   MFMA deliver V^T in exactly the key order of the S^T
 //                   result, so P never leaves registers.
 //   O^T accumulates with one query row per lane pair too, so the rescale by
-//   exp2(m_old - m_new) is a per-lane scalar.
+//   exp2(m_old - m_new) is a per-lane scalar. At the end O goes through LDS,
+//   so that every store instruction writes whole rows.
 // Offsets: every tensor base is formed in int64 (row * row_stride + head *
 // head_stride, as the "Suggested kernel-side fix" of the _bwd_preprocess page
 // asks) and rebased per tile; the per-lane buffer offsets inside a tile are
