@@ -239,6 +239,36 @@ def bench_backward(args) -> int:
     return 0
 
 
+# Operand patterns of the MFMA-rate stream. Each wave's operands are 8
+# fragments of 512 bf16 values (64 lanes x 8): fragments 0-3 are the A
+# operands, 4-7 the B operands.
+MFMA_OPERANDS = {
+    "random": "N(0,1) random bf16",
+    "ones": "all ones",
+    "uniform": "uniform [0, 1) random bf16",
+    "lane-constant": "N(0,1) random, one value per fragment (the same in every lane and element)",
+    "a-random-b-ones": "A N(0,1) random, B all ones",
+    "a-ones-b-random": "A all ones, B N(0,1) random",
+}
+
+
+def mfma_operands(mode: str, n: int, dev, g):
+    import torch
+
+    if mode == "ones":
+        return torch.ones(n, dtype=torch.bfloat16, device=dev)
+    if mode == "uniform":
+        return torch.rand(n, device=dev, generator=g).to(torch.bfloat16)
+    x = torch.randn(n, dtype=torch.bfloat16, device=dev, generator=g).view(-1, 8, 512)
+    if mode == "lane-constant":
+        x = x[:, :, :1].expand(-1, -1, 512)
+    elif mode == "a-random-b-ones":
+        x[:, 4:, :] = 1.0
+    elif mode == "a-ones-b-random":
+        x[:, :4, :] = 1.0
+    return x.contiguous().view(-1)
+
+
 def bench_mfma_rate(args, dev) -> int:
     """The rate a plain bf16 MFMA stream reaches on this GPU with the given
     operand values (the calibration kernel of libavf_probe.so): under the
@@ -266,8 +296,7 @@ def bench_mfma_rate(args, dev) -> int:
     iters = 400000           # about 0.1 s per launch
     n = P.avf_probe_operand_bytes(wgs) // 2
     g = torch.Generator(device=dev).manual_seed(0)
-    ops = (torch.randn(n, dtype=torch.bfloat16, device=dev, generator=g) if args.mfma_rate == "random"
-           else torch.ones(n, dtype=torch.bfloat16, device=dev))
+    ops = mfma_operands(args.mfma_rate, n, dev, g)
     out = torch.empty(P.avf_probe_output_bytes(wgs) // 4, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -289,7 +318,7 @@ def bench_mfma_rate(args, dev) -> int:
     flops = wgs * 4 * iters * 8 * 32768
     tf = flops / (ms / 1e3) / 1e12
     print(json.dumps({"metric": "bf16 MFMA rate of a plain v_mfma_f32_32x32x16_bf16 stream", "value": round(tf, 1),
-                      "unit": "TFLOP/s", "operands": "N(0,1) random bf16" if args.mfma_rate == "random" else "all ones",
+                      "unit": "TFLOP/s", "operands": MFMA_OPERANDS[args.mfma_rate],
                       "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "peak": PEAK_BF16_TFLOPS,
                       "ms_per_launch": round(ms, 3), "workgroups": wgs, "iters": iters, "compute_units": cus,
                       "steps": args.steps, "warmup": args.warmup}), flush=True)
@@ -373,9 +402,9 @@ def main() -> int:
                     help="the workload's q, k, v and out as head-major views (row stride D, head stride tokens*D)")
     ap.add_argument("--coissue", action="store_true",
                     help="time MFMA slots with v_fma_f32 / v_exp_f32 co-issued (probe library)")
-    ap.add_argument("--mfma-rate", choices=["random", "ones"], default=None,
+    ap.add_argument("--mfma-rate", choices=sorted(MFMA_OPERANDS), default=None,
                     help="only time the roofline calibration kernel: a plain stream of bf16 MFMAs "
-                         "(v_mfma_f32_32x32x16_bf16) on N(0,1) random or all-ones bf16 operands, two waves per SIMD")
+                         "(v_mfma_f32_32x32x16_bf16) on the given operand pattern, two waves per SIMD")
     ap.add_argument("--copy-rate", type=int, default=0, metavar="MIB",
                     help="only time a plain device-to-device copy of MIB MiB (--warmup, then --steps copies) and "
                          "print its read + write GB/s: the rate a plain stream reaches on this GPU")

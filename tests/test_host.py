@@ -576,3 +576,25 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert P.avf_probe_coissue(4, 0, fake, 0, 1, None) == -2    # no workgroups
     assert P.avf_probe_mfma(fake, fake, 1, 3, None) == -2       # odd iteration count
     assert P.avf_probe_mfma(ctypes.c_void_p(4097), fake, 1, 2, None) == -2  # misaligned operands
+
+
+def test_mfma_rate_operand_patterns():
+    """bench.py --mfma-rate operand patterns have the layout the probe kernel
+    reads: per wave 8 fragments of 512 bf16, A = fragments 0-3, B = 4-7."""
+    import torch
+
+    import bench
+
+    n = 2 * 8 * 512
+    g = torch.Generator().manual_seed(0)
+    for mode in bench.MFMA_OPERANDS:
+        x = bench.mfma_operands(mode, n, "cpu", torch.Generator().manual_seed(0))
+        assert x.dtype == torch.bfloat16 and x.numel() == n, mode
+    x = bench.mfma_operands("lane-constant", n, "cpu", g).view(-1, 8, 512)
+    assert torch.equal(x, x[:, :, :1].expand_as(x)) and x[:, :, 0].unique().numel() > 1
+    x = bench.mfma_operands("a-random-b-ones", n, "cpu", g).view(-1, 8, 512)
+    assert bool((x[:, 4:] == 1).all()) and x[:, :4].unique().numel() > 100
+    x = bench.mfma_operands("a-ones-b-random", n, "cpu", g).view(-1, 8, 512)
+    assert bool((x[:, :4] == 1).all()) and x[:, 4:].unique().numel() > 100
+    x = bench.mfma_operands("uniform", n, "cpu", g)
+    assert float(x.min()) >= 0.0 and float(x.max()) <= 1.0
